@@ -1,0 +1,36 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+Holds no arithmetic of the attention method: it only draws i.i.d. N(0, 1)
+values with a seeded CPU generator (order Q, K, V, dO), applies the workload's
+Q/K multiplier (an exact power of two) and rounds to the compute dtype (RNE).
+"""
+import torch
+
+_DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def torch_dtype(name):
+    return _DT[name]
+
+
+def make_inputs(B, H, N, d, dtype="bf16", seed=0, qk_mult=1.0, with_grad=True):
+    """Returns CPU tensors (q, k, v, do) of shape [B, H, N, d] in `dtype`."""
+    g = torch.Generator().manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    do = torch.randn(shape, generator=g, dtype=torch.float32) if with_grad else None
+    if qk_mult != 1.0:
+        q = q * qk_mult
+        k = k * qk_mult
+    dt = _DT[dtype]
+    out = [q.to(dt), k.to(dt), v.to(dt)]
+    out.append(None if do is None else do.to(dt))
+    return tuple(out)
+
+
+def config_inputs(cfg, with_grad=None):
+    if with_grad is None:
+        with_grad = cfg.backward
+    return make_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed, cfg.qk_mult, with_grad)
