@@ -1,0 +1,161 @@
+"""Python binding of libattn.so (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/attn.h.  PyTorch supplies device
+memory (tensors) and the stream (the current HIP stream of the tensors'
+device).  There is no fallback: if the library is missing or the tensors are
+not on a GPU, the calls raise.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+
+EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_workspace_bytes",
+            "attn_bwd", "attn_status_str", "attn_last_hip_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().attn_status_str(status).decode()
+        if status == ATTN_EHIP:
+            msg += f" (hipError {lib().attn_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def lib():
+    """Loads libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
+        L.attn_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
+        L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp]
+        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.attn_bwd_workspace_bytes.restype = sz
+        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, i, vp, sz, vp]
+        for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_main", "attn_bwd"):
+            getattr(L, name).restype = i
+        L.attn_status_str.argtypes = [i]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_last_hip_error.argtypes = []
+        L.attn_last_hip_error.restype = i
+        _lib = L
+    return _lib
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check_inputs(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("tensors must be on a GPU")
+        if t.device != dev:
+            raise ValueError("tensors on different devices")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != ATTN_OK:
+        raise AttnError(st, name)
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """O = softmax(scale Q K^T) V and LSE.  Returns (O, LSE)."""
+    B, H, N, d = _shape(q)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    _check_inputs(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_inputs(q, o, l)
+    _call("attn_fwd", _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, float(scale), int(bool(causal)),
+          _ptr(o), _ptr(l), _stream(q, stream))
+    return o, l
+
+
+def attn_bwd_workspace_bytes(B, H, N, d, grad_dtype=torch.float32):
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d, ATTN_BF16 if grad_dtype == torch.bfloat16 else ATTN_F32))
+
+
+def attn_bwd_preprocess(o, do, D=None, dq_acc=None, stream=None):
+    """D = rowsum(dO o O) (fp32 [B,H,N]) and dq_acc = 0 (fp32 [B,H,N,d])."""
+    B, H, N, d = _shape(o)
+    _check_inputs(o, do)
+    D = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if D is None else D
+    dq_acc = torch.empty((B, H, N, d), dtype=torch.float32, device=o.device) if dq_acc is None else dq_acc
+    _call("attn_bwd_preprocess", _ptr(o), _ptr(do), _dt(o), B, H, N, d, _ptr(D), _ptr(dq_acc),
+          _stream(o, stream))
+    return D, dq_acc
+
+
+def attn_bwd_main(q, k, v, do, lse, D, dq_acc, scale=None, causal=False, dk=None, dv=None, stream=None):
+    """dK, dV (fp32, written) and dQ added into dq_acc.  Returns (dq_acc, dK, dV)."""
+    B, H, N, d = _shape(q)
+    _check_inputs(q, k, v, do, lse, D, dq_acc)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dk = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    _call("attn_bwd_main", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
+          float(scale), int(bool(causal)), _ptr(dq_acc), _ptr(dk), _ptr(dv), _stream(q, stream))
+    return dq_acc, dk, dv
+
+
+def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, grad_dtype=torch.float32, workspace=None,
+             dq=None, dk=None, dv=None, stream=None):
+    """Full backward.  Returns (dQ, dK, dV) in grad_dtype."""
+    B, H, N, d = _shape(q)
+    _check_inputs(q, k, v, o, do, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    gdt = ATTN_BF16 if grad_dtype == torch.bfloat16 else ATTN_F32
+    need = attn_bwd_workspace_bytes(B, H, N, d, grad_dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    mk = lambda t: torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) if t is None else t
+    dq, dk, dv = mk(dq), mk(dk), mk(dv)
+    _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
+          float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), gdt, _ptr(workspace),
+          ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q, stream))
+    return dq, dk, dv

@@ -1,0 +1,127 @@
+// C ABI of libattn.so: argument validation and dispatch to the HIP launchers.
+// Every check runs before the first HIP call, so a rejected request enqueues
+// nothing and writes nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+attn_status check_shape(int B, int H, int N, int d)
+{
+    if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_EINVAL;
+    const long long total = (long long)B * H * N * d;
+    if (total >= (1LL << 31)) return ATTN_EINVAL;
+    if (d != 64 && d != 80 && d != 128) return ATTN_EUNSUPPORTED;
+    return ATTN_OK;
+}
+
+bool dtype_ok(attn_dtype dt) { return dt == ATTN_F32 || dt == ATTN_BF16; }
+
+attn_status from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return ATTN_OK;
+    g_last_hip_error = (int)e;
+    return ATTN_EHIP;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(attn_status s)
+{
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_EUNSUPPORTED: return "unsupported configuration";
+        case ATTN_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+attn_status attn_fwd(const void* Q, const void* K, const void* V, attn_dtype dt, int B, int H, int N, int d,
+                     float scale, int causal, void* O, float* LSE, void* stream)
+{
+    attn_status s = check_shape(B, H, N, d);
+    if (s != ATTN_OK) return s;
+    if (!dtype_ok(dt) || !isfinite(scale) || (causal != 0 && causal != 1)) return ATTN_EINVAL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return ATTN_EINVAL;
+    return from_hip(attn::launch_fwd(Q, K, V, O, LSE, dt == ATTN_BF16, B * H, N, d, scale, causal,
+                                     (hipStream_t)stream));
+}
+
+attn_status attn_bwd_preprocess(const void* O, const void* dO, attn_dtype dt, int B, int H, int N, int d,
+                                float* D, float* dQacc, void* stream)
+{
+    attn_status s = check_shape(B, H, N, d);
+    if (s != ATTN_OK) return s;
+    if (!dtype_ok(dt)) return ATTN_EINVAL;
+    if (!aligned16(O) || !aligned16(dO) || !aligned16(D) || !aligned16(dQacc)) return ATTN_EINVAL;
+    return from_hip(attn::launch_bwd_pre(O, dO, dt == ATTN_BF16, B * H, N, d, D, dQacc, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                          const float* D, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                          float* dQacc, float* dK, float* dV, void* stream)
+{
+    attn_status s = check_shape(B, H, N, d);
+    if (s != ATTN_OK) return s;
+    if (!dtype_ok(dt) || !isfinite(scale) || (causal != 0 && causal != 1)) return ATTN_EINVAL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) ||
+        !aligned16(D) || !aligned16(dQacc) || !aligned16(dK) || !aligned16(dV))
+        return ATTN_EINVAL;
+    return from_hip(attn::launch_bwd_main(Q, K, V, dO, LSE, D, dt == ATTN_BF16, B * H, N, d, scale, causal,
+                                          dQacc, dK, dV, false, (hipStream_t)stream));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype grad_dt)
+{
+    if (check_shape(B, H, N, d) == ATTN_EINVAL || !dtype_ok(grad_dt)) return 0;
+    const size_t rows = (size_t)B * H * N;
+    size_t bytes = round256(rows * sizeof(float));
+    if (grad_dt == ATTN_BF16) bytes += round256(rows * (size_t)d * sizeof(float));
+    return bytes;
+}
+
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                     void* dQ, void* dK, void* dV, attn_dtype grad_dt, void* workspace,
+                     size_t workspace_bytes, void* stream)
+{
+    attn_status s = check_shape(B, H, N, d);
+    if (s != ATTN_OK) return s;
+    if (!dtype_ok(dt) || !dtype_ok(grad_dt) || !isfinite(scale) || (causal != 0 && causal != 1))
+        return ATTN_EINVAL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+        !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
+        return ATTN_EINVAL;
+    if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, grad_dt)) return ATTN_EINVAL;
+
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf_in = dt == ATTN_BF16, bf_grad = grad_dt == ATTN_BF16;
+    const int BH = B * H;
+    const size_t rows = (size_t)BH * N;
+    float* Dd = static_cast<float*>(workspace);
+    float* dQacc = bf_grad ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * sizeof(float)))
+                           : static_cast<float*>(dQ);
+    attn_status r = from_hip(attn::launch_bwd_pre(O, dO, bf_in, BH, N, d, Dd, dQacc, st));
+    if (r != ATTN_OK) return r;
+    r = from_hip(attn::launch_bwd_main(Q, K, V, dO, LSE, Dd, bf_in, BH, N, d, scale, causal, dQacc, dK, dV,
+                                       bf_grad, st));
+    if (r != ATTN_OK) return r;
+    if (bf_grad) r = from_hip(attn::launch_f32_to_bf16(dQacc, dQ, (long)(rows * d), st));
+    return r;
+}
+
+}  // extern "C"

@@ -1,0 +1,527 @@
+// Backward kernels: D = rowsum(dO o O), then dQ, dK, dV by recomputation.
+//
+// What it follows: FlashAttention-2 review, 'core algorithm' answer, section 2
+// (3) Backward Pass -- recompute S and P from the saved statistics instead of
+// storing them, then dS, dQ = dS K, dK = dS^T Q, dV = P^T dO (read as the
+// softmax Jacobian dS = P o (dP - D) with D_i = dO_i . O_i, and with the
+// chain-rule factor `scale` on dQ and dK); '[LLM] Flash Attention' blog,
+// "Recomputation" (more FLOPs, fewer HBM accesses).  The loop order (one
+// workgroup per block of keys, iterating over query blocks, so dK and dV are
+// reduced on chip and written once) follows the FlashAttention-2 review's
+// point that the backward parallelises over the sequence with little
+// synchronisation between blocks (results answer, section 3 (2)).
+//
+// gfx950 mapping (workgroup = 4 waves; each wave owns 32 keys, BN = 128 keys):
+//   * S = Q K^T and dP = dO V^T with K and V fragments resident in registers:
+//     every accumulator lane holds ONE key and 16 queries, which is exactly the
+//     operand layout the two products that contract over queries need:
+//       dV^T += dO^T P   and   dK^T += Q^T dS   (accumulated in registers).
+//     Q^T and dO^T are staged transposed in LDS for those A operands.
+//   * P = exp2(S * scale * log2e - LSE * log2e): no max, no sum; LSE rows past N
+//     are +inf so their probabilities are exactly 0.
+//   * dQ needs dS with queries on lanes: each wave writes its dS columns to LDS
+//     once, then the workgroup computes dQ = dS K for its 128 keys (K^T kept in
+//     LDS for the whole pass) and adds it into an fp32 accumulator with
+//     hardware float atomics in L2 (coalesced: 32 lanes cover 32 consecutive
+//     head-dim columns of one row).
+//   * Causal: query blocks entirely above the workgroup's keys are never
+//     visited; a wave whose keys all lie after a block's last query skips its
+//     products and contributes zeros to dS.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+// ----------------------------------------------------------------------------
+// Preprocess: D_i = sum_k dO_ik O_ik (fp32) and dQacc = 0.  Memory bound.
+// 8 lanes per row, 32 rows per 256-thread block.
+// ----------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                                                      float* __restrict__ Dout,
+                                                      float* __restrict__ dQacc, long rows)
+{
+    constexpr int CH = Mma<T>::CH, CPR = D / CH, LPR = 8;
+    const long row = (long)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
+    const int u = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const T* o = O + row * D;
+        const T* g = dO + row * D;
+        for (int cidx = u; cidx < CPR; cidx += LPR) {
+            const u32x4 a = ld16(o + cidx * CH), b = ld16(g + cidx * CH);
+            if constexpr (sizeof(T) == 2) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf((float)av[e], (float)bv[e], acc);
+            } else {
+                const f32x4 av = __builtin_bit_cast(f32x4, a), bv = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = fmaf(av[e], bv[e], acc);
+            }
+        }
+        float* z = dQacc + row * D;
+        for (int x = u; x < D / 4; x += LPR) st16(z + 4 * x, zero4());
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && u == 0) Dout[row] = acc;
+}
+
+// ----------------------------------------------------------------------------
+// Main backward kernel.
+// ----------------------------------------------------------------------------
+template <typename T, int D>
+struct BwdCfg {
+    static constexpr int THREADS = 256;
+    static constexpr int BN = 128;                       // keys per workgroup (32 per wave)
+    static constexpr int BM = sizeof(T) == 2 ? 64 : 32;  // query rows per iteration
+    static constexpr int NQT = BM / 32;
+    static constexpr int DP = (D + 31) / 32 * 32;
+    static constexpr int NDT = DP / 32;
+    static constexpr int E = Mma<T>::E, KS = Mma<T>::KS, CH = Mma<T>::CH;
+    static constexpr int NKS = D / KS;                   // steps over the head dim
+    static constexpr int CPR = D / CH;
+    static constexpr int QPITCH = D + (sizeof(T) == 2 ? 8 : 4);   // Qs, dOs  [BM][QPITCH]
+    static constexpr int TPITCH = BM + 4;                         // Qt, dOt  [DP][TPITCH]
+    static constexpr int SPITCH = BN + (sizeof(T) == 2 ? 8 : 4);  // dS       [BM][SPITCH]
+    static constexpr int KTPITCH = BN + (sizeof(T) == 2 ? 8 : 4); // Kt       [DP][KTPITCH]
+    static constexpr int OFF_QS = 0;
+    static constexpr int OFF_DOS = OFF_QS + BM * QPITCH;
+    static constexpr int OFF_QT = OFF_DOS + BM * QPITCH;
+    static constexpr int OFF_DOT = OFF_QT + DP * TPITCH;
+    static constexpr int OFF_DS = OFF_DOT + DP * TPITCH;
+    static constexpr int OFF_KT = OFF_DS + BM * SPITCH;
+    static constexpr int ELEMS = OFF_KT + DP * KTPITCH;
+    static constexpr int BYTES = ELEMS * sizeof(T) + 2 * BM * sizeof(float);
+    static constexpr int QGROUPS = (BM / 4) * CPR;       // 4 rows x 1 chunk per group
+    static constexpr int QLD = (QGROUPS + THREADS - 1) / THREADS;
+    static constexpr int KGROUPS = (BN / 4) * CPR;
+    static constexpr int DQ_TILES = NQT * NDT;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(D % KS == 0 && D % CH == 0, "head dim");
+};
+
+// Transposed store of a 4-row x 1-chunk group: for each of the chunk's CH
+// columns, the 4 rows' values are written contiguously at dst[col][row0..row0+3].
+template <typename T>
+__device__ __forceinline__ void store_transposed4(T* base, int pitch, int col0, int row0, const u32x4 (&v)[4])
+{
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo0 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x05040100u);
+            const uint32_t lo1 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x05040100u);
+            const uint32_t hi0 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x07060302u);
+            const uint32_t hi1 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x07060302u);
+            *reinterpret_cast<u32x2*>(base + (col0 + 2 * w) * pitch + row0) = u32x2{lo0, lo1};
+            *reinterpret_cast<u32x2*>(base + (col0 + 2 * w + 1) * pitch + row0) = u32x2{hi0, hi1};
+        }
+    } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            st16(base + (col0 + x) * pitch + row0, u32x4{v[0][x], v[1][x], v[2][x], v[3][x]});
+    }
+}
+
+template <typename T, int D, bool CAUSAL, typename G>
+__global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                  const T* __restrict__ V, const T* __restrict__ dO,
+                                                  const float* __restrict__ LSE,
+                                                  const float* __restrict__ Dg,
+                                                  float* __restrict__ dQacc, G* __restrict__ dK,
+                                                  G* __restrict__ dV, int N, int nkblk, float scale)
+{
+    using C = BwdCfg<T, D>;
+    using M = Mma<T>;
+    typedef typename M::frag frag;
+
+    __shared__ __attribute__((aligned(16))) char smem_raw[C::BYTES];
+    T* smem = reinterpret_cast<T*>(smem_raw);
+    T* Qs = smem + C::OFF_QS;
+    T* dOs = smem + C::OFF_DOS;
+    T* Qt = smem + C::OFF_QT;
+    T* dOt = smem + C::OFF_DOT;
+    T* dSl = smem + C::OFF_DS;
+    T* Kt = smem + C::OFF_KT;
+    float* lse_l = reinterpret_cast<float*>(smem_raw + C::ELEMS * sizeof(T));
+    float* d_l = lse_l + C::BM;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = bid / nkblk;
+    const int kb = bid - head * nkblk;
+    const int k0 = kb * C::BN;
+    const int k0w = k0 + 32 * wave;            // this wave's first key
+    const int mykey = k0w + l32;
+    const size_t hoff = (size_t)head * (size_t)N * D;
+    const T* __restrict__ Qh = Q + hoff;
+    const T* __restrict__ Kh = K + hoff;
+    const T* __restrict__ Vh = V + hoff;
+    const T* __restrict__ dOh = dO + hoff;
+    const float* __restrict__ LSEh = LSE + (size_t)head * N;
+    const float* __restrict__ Dh = Dg + (size_t)head * N;
+    float* __restrict__ dQh = dQacc + hoff;
+
+    const float c2 = scale * kLog2e;
+
+    // ---- resident K, V fragments (B operands of S = Q K^T and dP = dO V^T) ----
+    frag kf[C::NKS], vf[C::NKS];
+#pragma unroll
+    for (int s = 0; s < C::NKS; ++s) {
+        if constexpr (sizeof(T) == 2) {
+            const bool ok = mykey < N;
+            kf[s] = __builtin_bit_cast(bf16x8, ok ? ld16(Kh + (size_t)mykey * D + s * C::KS + C::E * h) : zero4());
+            vf[s] = __builtin_bit_cast(bf16x8, ok ? ld16(Vh + (size_t)mykey * D + s * C::KS + C::E * h) : zero4());
+        } else {
+            const bool ok = mykey < N;
+            kf[s] = ok ? Kh[(size_t)mykey * D + s * C::KS + h] : 0.f;
+            vf[s] = ok ? Vh[(size_t)mykey * D + s * C::KS + h] : 0.f;
+        }
+    }
+
+    // ---- K^T of the workgroup's keys in LDS (B operand of dQ = dS K); pad rows zeroed ----
+    for (int f = tid; f < C::KGROUPS; f += C::THREADS) {
+        const int g = f / C::CPR, col = f - g * C::CPR;
+        u32x4 v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = k0 + 4 * g + e;
+            v[e] = key < N ? ld16(Kh + (size_t)key * D + col * C::CH) : zero4();
+        }
+        store_transposed4<T>(Kt, C::KTPITCH, col * C::CH, 4 * g, v);
+    }
+    if constexpr (C::DP > D) {
+        for (int x = tid; x < (C::DP - D) * C::KTPITCH; x += C::THREADS) Kt[D * C::KTPITCH + x] = from_f32<T>(0.f);
+        for (int x = tid; x < (C::DP - D) * C::TPITCH; x += C::THREADS) {
+            Qt[D * C::TPITCH + x] = from_f32<T>(0.f);
+            dOt[D * C::TPITCH + x] = from_f32<T>(0.f);
+        }
+    }
+
+    f32x16 dvacc[C::NDT], dkacc[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dvacc[dt][r] = 0.f; dkacc[dt][r] = 0.f; }
+
+    const int nq = (N + C::BM - 1) / C::BM;
+    const int i0 = CAUSAL ? (k0 / C::BM) : 0;
+
+    // ---- staging of one query block: Q, dO (4-row groups), LSE*log2e, D ----
+    u32x4 qst[C::QLD][4], gst[C::QLD][4];
+    float lst = 0.f, dst_ = 0.f;
+    auto load_q = [&](int i) {
+        const int q0 = i * C::BM;
+#pragma unroll
+        for (int it = 0; it < C::QLD; ++it) {
+            const int f = tid + C::THREADS * it;
+            if (f < C::QGROUPS) {
+                const int g = f / C::CPR, col = f - g * C::CPR;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int q = q0 + 4 * g + e;
+                    const bool ok = q < N;
+                    qst[it][e] = ok ? ld16(Qh + (size_t)q * D + col * C::CH) : zero4();
+                    gst[it][e] = ok ? ld16(dOh + (size_t)q * D + col * C::CH) : zero4();
+                }
+            }
+        }
+        if (tid < C::BM) {
+            const int q = q0 + tid;
+            lst = q < N ? LSEh[q] * kLog2e : __builtin_inff();
+            dst_ = q < N ? Dh[q] : 0.f;
+        }
+    };
+    auto store_q = [&]() {
+#pragma unroll
+        for (int it = 0; it < C::QLD; ++it) {
+            const int f = tid + C::THREADS * it;
+            if (f < C::QGROUPS) {
+                const int g = f / C::CPR, col = f - g * C::CPR;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    st16(Qs + (4 * g + e) * C::QPITCH + col * C::CH, qst[it][e]);
+                    st16(dOs + (4 * g + e) * C::QPITCH + col * C::CH, gst[it][e]);
+                }
+                store_transposed4<T>(Qt, C::TPITCH, col * C::CH, 4 * g, qst[it]);
+                store_transposed4<T>(dOt, C::TPITCH, col * C::CH, 4 * g, gst[it]);
+            }
+        }
+        if (tid < C::BM) { lse_l[tid] = lst; d_l[tid] = dst_; }
+    };
+
+    if (i0 < nq) load_q(i0);
+    for (int i = i0; i < nq; ++i) {
+        const int q0 = i * C::BM;
+        __syncthreads();                 // previous iteration's LDS readers are done
+        store_q();
+        __syncthreads();
+        if (i + 1 < nq) load_q(i + 1);
+
+        const bool skip = CAUSAL && (k0w > q0 + C::BM - 1);   // all of this wave's keys after the block
+        if (skip) {
+            // contribute zeros to the dS tile the dQ product reads
+            for (int x = lane; x < C::BM; x += 64) {
+                T* row = dSl + x * C::SPITCH + 32 * wave;
+#pragma unroll
+                for (int y = 0; y < 32; ++y) row[y] = from_f32<T>(0.f);
+            }
+        } else {
+            const bool need_mask = (CAUSAL && q0 < k0w + 31) || (q0 + C::BM > N) || (k0w + 32 > N);
+            f32x16 sacc[C::NQT], pacc[C::NQT];
+#pragma unroll
+            for (int qt = 0; qt < C::NQT; ++qt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { sacc[qt][r] = 0.f; pacc[qt][r] = 0.f; }
+            // S = Q K^T, dP = dO V^T
+#pragma unroll
+            for (int s = 0; s < C::NKS; ++s) {
+#pragma unroll
+                for (int qt = 0; qt < C::NQT; ++qt) {
+                    const int off = (32 * qt + l32) * C::QPITCH + s * C::KS + C::E * h;
+                    frag a, g;
+                    if constexpr (sizeof(T) == 2) {
+                        a = __builtin_bit_cast(bf16x8, ld16(Qs + off));
+                        g = __builtin_bit_cast(bf16x8, ld16(dOs + off));
+                    } else {
+                        a = Qs[off];
+                        g = dOs[off];
+                    }
+                    sacc[qt] = M::mma(a, kf[s], sacc[qt]);
+                    pacc[qt] = M::mma(g, vf[s], pacc[qt]);
+                }
+            }
+            // P = exp2(S c2 - LSE log2e); dS = P o (dP - D)   (sacc <- P, pacc <- dS)
+#pragma unroll
+            for (int qt = 0; qt < C::NQT; ++qt) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int qo = 32 * qt + 8 * g4 + 4 * h;
+                    const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_l + qo);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_l + qo);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g4 + e;
+                        float p = fast_exp2(fmaf(sacc[qt][r], c2, -lse4[e]));
+                        if (need_mask) {
+                            const int q = q0 + qo + e;
+                            if ((CAUSAL && mykey > q) || mykey >= N) p = 0.f;
+                        }
+                        sacc[qt][r] = p;
+                        pacc[qt][r] = p * (pacc[qt][r] - d4[e]);
+                    }
+                }
+            }
+            // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over the block's queries)
+#pragma unroll
+            for (int qt = 0; qt < C::NQT; ++qt) {
+#pragma unroll
+                for (int s2 = 0; s2 < 32 / C::KS; ++s2) {
+                    frag bp, bs;
+                    if constexpr (sizeof(T) == 2) {
+                        bf16x8 x, y;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            x[e] = to_bf16(sacc[qt][8 * s2 + e]);
+                            y[e] = to_bf16(pacc[qt][8 * s2 + e]);
+                        }
+                        bp = x;
+                        bs = y;
+                    } else {
+                        bp = sacc[qt][s2];
+                        bs = pacc[qt][s2];
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) {
+                        const int rowoff = (32 * dt + l32) * C::TPITCH + 32 * qt;
+                        frag ag, aq;
+                        if constexpr (sizeof(T) == 2) {
+                            const int o0 = rowoff + 16 * s2 + 4 * h, o1 = o0 + 8;
+                            const u32x2 g0 = *reinterpret_cast<const u32x2*>(dOt + o0);
+                            const u32x2 g1 = *reinterpret_cast<const u32x2*>(dOt + o1);
+                            const u32x2 q0v = *reinterpret_cast<const u32x2*>(Qt + o0);
+                            const u32x2 q1v = *reinterpret_cast<const u32x2*>(Qt + o1);
+                            ag = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
+                            aq = __builtin_bit_cast(bf16x8, u32x4{q0v[0], q0v[1], q1v[0], q1v[1]});
+                        } else {
+                            const int o = rowoff + 8 * (s2 >> 2) + 4 * h + (s2 & 3);
+                            ag = dOt[o];
+                            aq = Qt[o];
+                        }
+                        dvacc[dt] = M::mma(ag, bp, dvacc[dt]);
+                        dkacc[dt] = M::mma(aq, bs, dkacc[dt]);
+                    }
+                }
+            }
+            // dS -> LDS as [query][key] for the dQ product
+#pragma unroll
+            for (int qt = 0; qt < C::NQT; ++qt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qo = 32 * qt + 8 * (r >> 2) + 4 * h + (r & 3);
+                    dSl[qo * C::SPITCH + 32 * wave + l32] = from_f32<T>(pacc[qt][r]);
+                }
+        }
+        __syncthreads();
+        // dQ[q][d] += scale * sum_key dS[q][key] K[key][d]  (tiles of 32 q x 32 d)
+        for (int tile = wave; tile < C::DQ_TILES; tile += 4) {
+            const int qt = tile % C::NQT, dt = tile / C::NQT;
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < C::BN / C::KS; ++s) {
+                const T* pa = dSl + (32 * qt + l32) * C::SPITCH + s * C::KS + C::E * h;
+                const T* pb = Kt + (32 * dt + l32) * C::KTPITCH + s * C::KS + C::E * h;
+                frag a, b;
+                if constexpr (sizeof(T) == 2) {
+                    a = __builtin_bit_cast(bf16x8, ld16(pa));
+                    b = __builtin_bit_cast(bf16x8, ld16(pb));
+                } else {
+                    a = *pa;
+                    b = *pb;
+                }
+                acc = M::mma(a, b, acc);
+            }
+            const int dcol = 32 * dt + l32;
+            if (dcol < D) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int q = q0 + 32 * qt + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (q < N) unsafeAtomicAdd(dQh + (size_t)q * D + dcol, acc[r] * scale);
+                }
+            }
+        }
+    }
+
+    // ---- dK = scale * dK^T acc, dV = dV^T acc, written once ----
+    if (mykey < N) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * dt + 8 * g4 + 4 * h;
+                if (d0 < D) {
+                    G* pk = dK + hoff + (size_t)mykey * D + d0;
+                    G* pv = dV + hoff + (size_t)mykey * D + d0;
+                    if constexpr (sizeof(G) == 4) {
+                        f32x4 a, b;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { a[e] = dkacc[dt][4 * g4 + e] * scale; b[e] = dvacc[dt][4 * g4 + e]; }
+                        *reinterpret_cast<f32x4*>(pk) = a;
+                        *reinterpret_cast<f32x4*>(pv) = b;
+                    } else {
+                        bf16x4 a, b;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { a[e] = to_bf16(dkacc[dt][4 * g4 + e] * scale); b[e] = to_bf16(dvacc[dt][4 * g4 + e]); }
+                        *reinterpret_cast<bf16x4*>(pk) = a;
+                        *reinterpret_cast<bf16x4*>(pv) = b;
+                    }
+                }
+            }
+    }
+}
+
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, long n4)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * i);
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = to_bf16(v[e]);
+        *reinterpret_cast<bf16x4*>(dst + 4 * i) = o;
+    }
+}
+
+// ----------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------
+template <typename T, int D>
+static hipError_t pre_t(const void* O, const void* dO, int BH, int N, float* Dd, float* dQacc, hipStream_t st)
+{
+    const long rows = (long)BH * N;
+    const long blocks = (rows + 31) / 32;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, (const T*)O,
+                       (const T*)dO, Dd, dQacc, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const void* O, const void* dO, bool bf16_in, int BH, int N, int d, float* Dd,
+                          float* dQacc, hipStream_t st)
+{
+    if (bf16_in) {
+        switch (d) {
+            case 64: return pre_t<bf16, 64>(O, dO, BH, N, Dd, dQacc, st);
+            case 80: return pre_t<bf16, 80>(O, dO, BH, N, Dd, dQacc, st);
+            case 128: return pre_t<bf16, 128>(O, dO, BH, N, Dd, dQacc, st);
+        }
+    } else {
+        switch (d) {
+            case 64: return pre_t<float, 64>(O, dO, BH, N, Dd, dQacc, st);
+            case 80: return pre_t<float, 80>(O, dO, BH, N, Dd, dQacc, st);
+            case 128: return pre_t<float, 128>(O, dO, BH, N, Dd, dQacc, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int D, bool CAUSAL, typename G>
+static hipError_t main_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                         const float* Dd, int BH, int N, float scale, float* dQacc, void* dK, void* dV,
+                         hipStream_t st)
+{
+    using C = BwdCfg<T, D>;
+    const int nkblk = (N + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL, G>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, LSE, Dd, dQacc, (G*)dK,
+                       (G*)dV, N, nkblk, scale);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t main_d(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                         const float* Dd, int BH, int N, float scale, int causal, float* dQacc, void* dK,
+                         void* dV, bool bf16_grad, hipStream_t st)
+{
+    if (causal) {
+        if (bf16_grad) return main_t<T, D, true, bf16>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+        return main_t<T, D, true, float>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+    }
+    if (bf16_grad) return main_t<T, D, false, bf16>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+    return main_t<T, D, false, float>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+}
+
+hipError_t launch_bwd_main(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                           const float* Dd, bool bf16_in, int BH, int N, int d, float scale, int causal,
+                           float* dQacc, void* dK, void* dV, bool bf16_grad, hipStream_t st)
+{
+    if (bf16_in) {
+        switch (d) {
+            case 64: return main_d<bf16, 64>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
+            case 80: return main_d<bf16, 80>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
+            case 128: return main_d<bf16, 128>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
+        }
+    } else {
+        switch (d) {
+            case 64: return main_d<float, 64>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
+            case 80: return main_d<float, 80>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
+            case 128: return main_d<float, 128>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_f32_to_bf16(const float* src, void* dst, long n, hipStream_t st)
+{
+    const long n4 = n / 4;
+    if (n4 > 0)
+        hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, src,
+                           (bf16*)dst, n4);
+    return hipGetLastError();
+}
+
+}  // namespace attn

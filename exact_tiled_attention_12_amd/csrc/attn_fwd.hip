@@ -1,0 +1,401 @@
+// Forward kernel: O = softmax(scale Q K^T) V and LSE, one fused pass.
+//
+// What it follows: FlashAttention-2 review, 'core algorithm' answer, section 2
+// (1) tiling into T_r row blocks and T_c column blocks, (2) per-block S, P and
+// P V with the running max m and running sum l, (3) one final adjustment;
+// "IO-4 FlashAttention", sections 3-4 (block algorithm, online softmax).
+// Split-Q work partitioning (each wave owns its own query rows and never
+// exchanges partial results with other waves): FlashAttention-2 review, the
+// Split-K vs Split-Q answer, section 2.
+//
+// gfx950 mapping (one workgroup = 4 waves = 256 threads per block of BM query
+// rows; each wave owns 32*QT rows):
+//   * The wave computes S^T = K Q^T with bf16 MFMA 32x32x16 (fp32 MFMA
+//     32x32x2 for fp32 inputs), so every lane of the accumulator holds ONE
+//     query and 16 keys.  The running max, running sum and rescale factor are
+//     then per-lane scalars; the only cross-lane step per tile is one exchange
+//     with lane l^32, which holds the other 16 keys of the same query.
+//   * O^T = V^T P^T: the S^T accumulator registers, rounded to bf16, ARE the
+//     B operand of the next MFMA (the contraction over keys is permuted to the
+//     accumulator's row order, and V^T is read with the same permutation).
+//   * K tiles are staged row-major in LDS, V tiles transposed (key fastest)
+//     so that each lane reads its 4+4 keys with two 8-byte LDS reads.  Both
+//     are double-buffered; the next tile's global loads are in flight while
+//     the current tile is multiplied (one barrier per tile).
+//   * Causal: column tiles entirely above the block's diagonal are never
+//     loaded; tiles entirely above a wave's own rows are skipped by that wave;
+//     the element mask runs only on tiles that cross the diagonal or N.
+//   * Blocks of one head run on one XCD (shared L2 for its K, V); with a
+//     causal mask the heaviest row blocks of a head start first.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+template <typename T, int D, int QT>
+struct FwdCfg {
+    static constexpr int THREADS = 256;
+    static constexpr int BM = 4 * 32 * QT;          // query rows per workgroup
+    static constexpr int BN = 64;                   // keys per tile
+    static constexpr int NKT = BN / 32;             // 32-key sub-tiles
+    static constexpr int DP = (D + 31) / 32 * 32;   // head dim padded to the 32-row O^T tiles
+    static constexpr int NDT = DP / 32;
+    static constexpr int E = Mma<T>::E, KS = Mma<T>::KS, CH = Mma<T>::CH;
+    static constexpr int NKS = D / KS;              // MFMA steps of the Q K^T contraction
+    static constexpr int KPITCH = D + (sizeof(T) == 2 ? 8 : 4);   // elements; conflict-free b128 reads
+    static constexpr int VPITCH = BN + 4;                         // elements
+    static constexpr int KBUF = BN * KPITCH;
+    static constexpr int VBUF = DP * VPITCH;
+    static constexpr int CPR = D / CH;              // 16-byte chunks per row
+    static constexpr int KCHUNKS = BN * CPR;
+    static constexpr int KLD = (KCHUNKS + THREADS - 1) / THREADS;
+    static constexpr int VGROUPS = (BN / 4) * CPR;  // 4 keys x 1 chunk each
+    static constexpr int VLD = (VGROUPS + THREADS - 1) / THREADS;
+    static constexpr int SMEM_ELEMS = 2 * (KBUF + VBUF);
+    static_assert(D % KS == 0, "head dim must be a multiple of the MFMA contraction");
+    static_assert(D % CH == 0, "head dim must be a multiple of the chunk size");
+    static_assert(SMEM_ELEMS * sizeof(T) <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int D, bool CAUSAL, int QT>
+__global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                  const T* __restrict__ V, T* __restrict__ O,
+                                                  float* __restrict__ LSE, int N, int nqblk, float c,
+                                                  int negate_q)
+{
+    using C = FwdCfg<T, D, QT>;
+    using M = Mma<T>;
+    typedef typename M::frag frag;
+    constexpr float NEG_INF = -__builtin_inff();
+
+    __shared__ __attribute__((aligned(16))) T smem[C::SMEM_ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = bid / nqblk;
+    int qb = bid - head * nqblk;
+    if (CAUSAL) qb = nqblk - 1 - qb;                 // heavy row blocks first
+    const int q0 = qb * C::BM;
+    const int q0w = q0 + wave * 32 * QT;             // this wave's first query row
+    const size_t hoff = (size_t)head * (size_t)N * D;
+    const T* __restrict__ Qh = Q + hoff;
+    const T* __restrict__ Kh = K + hoff;
+    const T* __restrict__ Vh = V + hoff;
+
+    // ---- Q fragments (B operand of S^T = K Q^T), held for the whole pass ----
+    frag qf[QT][C::NKS];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        const int q = q0w + 32 * t + l32;
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+            if constexpr (sizeof(T) == 2) {
+                u32x4 raw = q < N ? ld16(Qh + (size_t)q * D + s * C::KS + C::E * h) : zero4();
+                if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+                qf[t][s] = __builtin_bit_cast(bf16x8, raw);
+            } else {
+                float x = q < N ? Qh[(size_t)q * D + s * C::KS + h] : 0.f;
+                qf[t][s] = negate_q ? -x : x;
+            }
+        }
+    }
+
+    // Rows D..DP-1 of the V^T buffers feed only discarded output rows; zero them once.
+    if constexpr (C::DP > D) {
+        for (int b = 0; b < 2; ++b) {
+            T* Vl = smem + b * (C::KBUF + C::VBUF) + C::KBUF;
+            for (int x = tid; x < (C::DP - D) * C::VPITCH; x += C::THREADS)
+                Vl[D * C::VPITCH + x] = from_f32<T>(0.f);
+        }
+    }
+
+    f32x16 oacc[C::NDT][QT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][t][r] = 0.f;
+    float m[QT], l[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) { m[t] = NEG_INF; l[t] = 0.f; }
+
+    const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+    const int ntiles = (kv_end + C::BN - 1) / C::BN;
+
+    // ---- staging: global -> registers -> LDS ----
+    u32x4 kst[C::KLD];
+    u32x4 vst[C::VLD][4];
+    auto load_tile = [&](int j) {
+        const int kv0 = j * C::BN;
+#pragma unroll
+        for (int i = 0; i < C::KLD; ++i) {
+            const int f = tid + C::THREADS * i;
+            if (f < C::KCHUNKS) {
+                const int row = f / C::CPR, col = f - row * C::CPR;
+                const int key = kv0 + row;
+                kst[i] = key < N ? ld16(Kh + (size_t)key * D + col * C::CH) : zero4();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::VLD; ++i) {
+            const int f = tid + C::THREADS * i;
+            if (f < C::VGROUPS) {
+                const int g = f / C::CPR, col = f - g * C::CPR;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = kv0 + 4 * g + e;
+                    vst[i][e] = key < N ? ld16(Vh + (size_t)key * D + col * C::CH) : zero4();
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        T* Kl = smem + buf * (C::KBUF + C::VBUF);
+        T* Vl = Kl + C::KBUF;
+#pragma unroll
+        for (int i = 0; i < C::KLD; ++i) {
+            const int f = tid + C::THREADS * i;
+            if (f < C::KCHUNKS) {
+                const int row = f / C::CPR, col = f - row * C::CPR;
+                st16(Kl + row * C::KPITCH + col * C::CH, kst[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::VLD; ++i) {
+            const int f = tid + C::THREADS * i;
+            if (f < C::VGROUPS) {
+                const int g = f / C::CPR, col = f - g * C::CPR;
+                if constexpr (sizeof(T) == 2) {
+                    // 4 keys x 8 head-dim values -> for each of the 8 dims, 4 keys (8 bytes).
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t lo0 = __builtin_amdgcn_perm(vst[i][1][w], vst[i][0][w], 0x05040100u);
+                        const uint32_t lo1 = __builtin_amdgcn_perm(vst[i][3][w], vst[i][2][w], 0x05040100u);
+                        const uint32_t hi0 = __builtin_amdgcn_perm(vst[i][1][w], vst[i][0][w], 0x07060302u);
+                        const uint32_t hi1 = __builtin_amdgcn_perm(vst[i][3][w], vst[i][2][w], 0x07060302u);
+                        const int dd = col * C::CH + 2 * w;
+                        *reinterpret_cast<u32x2*>(Vl + dd * C::VPITCH + 4 * g) = u32x2{lo0, lo1};
+                        *reinterpret_cast<u32x2*>(Vl + (dd + 1) * C::VPITCH + 4 * g) = u32x2{hi0, hi1};
+                    }
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int dd = col * C::CH + x;
+                        st16(Vl + dd * C::VPITCH + 4 * g,
+                             u32x4{vst[i][0][x], vst[i][1][x], vst[i][2][x], vst[i][3][x]});
+                    }
+                }
+            }
+        }
+    };
+
+    load_tile(0);
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        store_tile(buf);
+        __syncthreads();
+        if (j + 1 < ntiles) load_tile(j + 1);
+
+        const int kv0 = j * C::BN;
+        if (CAUSAL && kv0 > q0w + 32 * QT - 1) continue;     // every key is above this wave's rows
+
+        const T* Kl = smem + buf * (C::KBUF + C::VBUF);
+        const T* Vl = Kl + C::KBUF;
+
+        // ---- S^T = K Q^T (raw dot products; the scale is folded into the exponent) ----
+        f32x16 sacc[C::NKT][QT];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int t = 0; t < QT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kt][t][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt) {
+                const T* src = Kl + (32 * kt + l32) * C::KPITCH + s * C::KS + C::E * h;
+                frag a;
+                if constexpr (sizeof(T) == 2) a = __builtin_bit_cast(bf16x8, ld16(src));
+                else a = *src;
+#pragma unroll
+                for (int t = 0; t < QT; ++t) sacc[kt][t] = M::mma(a, qf[t][s], sacc[kt][t]);
+            }
+        }
+
+        // ---- online softmax (per lane: one query, 16 keys per sub-tile) ----
+        const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > q0w) || (kv0 + C::BN > N);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            const int q = q0w + 32 * t + l32;
+            float mx = NEG_INF;
+            if (need_mask) {
+#pragma unroll
+                for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const bool dead = (CAUSAL && key > q) || key >= N;
+                        if (dead) sacc[kt][t][r] = NEG_INF;
+                        mx = fmaxf(mx, sacc[kt][t][r]);
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][t][r]);
+            }
+            mx = fmaxf(mx, xor32(mx));
+            const float mnew = fmaxf(m[t], mx);
+            const float ms = (mnew == NEG_INF) ? 0.f : mnew * c;
+            const float alpha = (m[t] == NEG_INF) ? 0.f : fast_exp2(fmaf(m[t], c, -ms));
+            float rs = 0.f;
+            if (need_mask) {
+#pragma unroll
+                for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float sv = sacc[kt][t][r];
+                        const float p = (sv == NEG_INF) ? 0.f : fast_exp2(fmaf(sv, c, -ms));
+                        sacc[kt][t][r] = p;
+                        rs += p;
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = fast_exp2(fmaf(sacc[kt][t][r], c, -ms));
+                        sacc[kt][t][r] = p;
+                        rs += p;
+                    }
+            }
+            l[t] = fmaf(l[t], alpha, rs);
+            m[t] = mnew;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][t][r] *= alpha;
+        }
+
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt) {
+#pragma unroll
+            for (int s2 = 0; s2 < 32 / C::KS; ++s2) {
+                frag b[QT];
+#pragma unroll
+                for (int t = 0; t < QT; ++t) {
+                    if constexpr (sizeof(T) == 2) {
+                        bf16x8 pb;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pb[e] = to_bf16(sacc[kt][t][8 * s2 + e]);
+                        b[t] = pb;
+                    } else {
+                        b[t] = sacc[kt][t][s2];
+                    }
+                }
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt) {
+                    const T* vrow = Vl + (32 * dt + l32) * C::VPITCH + 32 * kt;
+                    frag a;
+                    if constexpr (sizeof(T) == 2) {
+                        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 4 * h);
+                        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 8 + 4 * h);
+                        a = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+                    } else {
+                        a = vrow[8 * (s2 >> 2) + 4 * h + (s2 & 3)];
+                    }
+#pragma unroll
+                    for (int t = 0; t < QT; ++t) oacc[dt][t] = M::mma(a, b[t], oacc[dt][t]);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: one division by l, O and LSE written once ----
+    T* Oh = O + hoff;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+        const float lt = l[t] + xor32(l[t]);
+        const float inv = 1.0f / lt;
+        const int q = q0w + 32 * t + l32;
+        if (q < N) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = 32 * dt + 8 * g + 4 * h;
+                    if (d0 < D) {
+                        T* dst = Oh + (size_t)q * D + d0;
+                        if constexpr (sizeof(T) == 2) {
+                            bf16x4 v;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = to_bf16(oacc[dt][t][4 * g + e] * inv);
+                            *reinterpret_cast<bf16x4*>(dst) = v;
+                        } else {
+                            f32x4 v;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) v[e] = oacc[dt][t][4 * g + e] * inv;
+                            *reinterpret_cast<f32x4*>(dst) = v;
+                        }
+                    }
+                }
+            if (h == 0) LSE[(size_t)head * N + q] = (m[t] * c + __log2f(lt)) * kLn2;
+        }
+    }
+}
+
+template <typename T, int D, bool CAUSAL, int QT>
+static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int BH, int N, float scale, hipStream_t st)
+{
+    using C = FwdCfg<T, D, QT>;
+    const int nqblk = (N + C::BM - 1) / C::BM;
+    const float c = fabsf(scale) * kLog2e;
+    const int negq = scale < 0.f;
+    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, QT>), dim3(nqblk * BH), dim3(C::THREADS), 0, st,
+                       (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, nqblk, c, negq);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int BH, int N, float scale, int causal, hipStream_t st)
+{
+    // Two query tiles per wave (BM = 256) halve the LDS reads per MFMA; use them
+    // when the grid still has enough workgroups to fill 256 CUs.
+    constexpr bool big_ok = sizeof(T) == 2;
+    const long wg_big = (long)BH * ((N + 255) / 256);
+    const bool big = big_ok && wg_big >= 256;
+    if (causal) {
+        if (big) return launch_fwd_t<T, D, true, big_ok ? 2 : 1>(Q, K, V, O, LSE, BH, N, scale, st);
+        return launch_fwd_t<T, D, true, 1>(Q, K, V, O, LSE, BH, N, scale, st);
+    }
+    if (big) return launch_fwd_t<T, D, false, big_ok ? 2 : 1>(Q, K, V, O, LSE, BH, N, scale, st);
+    return launch_fwd_t<T, D, false, 1>(Q, K, V, O, LSE, BH, N, scale, st);
+}
+
+hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, bool bf16_in,
+                      int BH, int N, int d, float scale, int causal, hipStream_t st)
+{
+    if (bf16_in) {
+        switch (d) {
+            case 64: return launch_fwd_d<bf16, 64>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+            case 80: return launch_fwd_d<bf16, 80>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+            case 128: return launch_fwd_d<bf16, 128>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+        }
+    } else {
+        switch (d) {
+            case 64: return launch_fwd_d<float, 64>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+            case 80: return launch_fwd_d<float, 80>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+            case 128: return launch_fwd_d<float, 128>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

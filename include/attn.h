@@ -1,0 +1,111 @@
+/*
+ * attn.h -- C ABI of the exact tiled attention library (libattn.so, gfx950).
+ *
+ * The operation (per head, Q, K, V in R^{N x d}):
+ *     S = scale * Q K^T,  P = softmax(S) row-wise,  O = P V,
+ *     LSE_i = log(sum_j exp(S_ij))             (natural log of the scaled scores)
+ * "IO-4 FlashAttention", problem setup (softmax(QK^T/sqrt(d_k))V) and section 1;
+ * FlashAttention-2 review, 'core algorithm' answer, section 1.  With causal = 1,
+ * key j is masked for query i when j > i (the plainest reading; the pages do not
+ * define a mask).
+ *
+ * The gradients of L = sum(dO o O), FlashAttention-2 review, 'core algorithm'
+ * answer, section 2 (3) Backward Pass, read as the softmax Jacobian:
+ *     dP = dO V^T,  D_i = sum_k dO_ik O_ik,  dS = P o (dP - D),
+ *     dV = P^T dO,  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Conventions shared by every entry point
+ *   - Q, K, V, O, dO, dQ, dK, dV are device pointers to contiguous row-major
+ *     [B, H, N, d] arrays (d fastest).  LSE and D are device fp32 [B, H, N].
+ *   - d must be 64, 80 or 128 (else ATTN_EUNSUPPORTED).  B, H, N >= 1 and
+ *     B*H*N*d < 2^31 (else ATTN_EINVAL).  Q, K, V have the same N.
+ *   - scale must be finite (else ATTN_EINVAL); its sign is arbitrary.
+ *   - Every pointer must be non-NULL and 16-byte aligned (else ATTN_EINVAL).
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without synchronising.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises, and keeps no state between calls apart from a
+ *     thread-local copy of the last HIP error.
+ *   - On ATTN_EINVAL / ATTN_EUNSUPPORTED nothing has been enqueued and no
+ *     output has been written.  On ATTN_EHIP (a launch failed) the outputs are
+ *     undefined and attn_last_hip_error() returns the hipError_t.  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = 1,        /* bad pointer, size, alignment, scale or flag   */
+    ATTN_EUNSUPPORTED = 2,  /* valid request the library does not implement */
+    ATTN_EHIP = 3           /* a HIP runtime call failed                     */
+} attn_status;
+
+typedef enum {
+    ATTN_F32 = 0,           /* IEEE binary32                                 */
+    ATTN_BF16 = 1           /* bfloat16 (8-bit exponent, 7-bit mantissa)     */
+} attn_dtype;
+
+/* Forward.  Q, K, V: inputs of dtype `dt`.  O: output of dtype `dt` (written
+ * once, rounded to nearest even when dt = ATTN_BF16).  LSE: fp32 output, the
+ * saved row statistic the backward recomputes P from (FlashAttention-2 review,
+ * 'core algorithm' answer, section 2 (3), item 1: the stored m and l, folded
+ * into LSE = m + ln l).  Scores and probabilities stay on chip; nothing of
+ * size N x N is written (FlashAttention-2 review, strengths answer: O(N)
+ * extra memory).  Arithmetic: products of dt values accumulated in fp32; the
+ * probabilities P are rounded to dt before the P V product. */
+attn_status attn_fwd(const void* Q, const void* K, const void* V, attn_dtype dt,
+                     int B, int H, int N, int d, float scale, int causal,
+                     void* O, float* LSE, void* stream);
+
+/* Backward preprocess: D_i = sum_k dO_ik O_ik in fp32 (the row-wise inner
+ * product the corrected dS formula needs), and dQacc = 0.  O, dO: dtype `dt`.
+ * D: fp32 [B,H,N] output.  dQacc: fp32 [B,H,N,d] output, zero-filled. */
+attn_status attn_bwd_preprocess(const void* O, const void* dO, attn_dtype dt,
+                                int B, int H, int N, int d,
+                                float* D, float* dQacc, void* stream);
+
+/* Backward main pass: one workgroup per block of keys; recomputes S and P
+ * from Q, K and the saved LSE ("Recomputation", '[LLM] Flash Attention' blog;
+ * FlashAttention-2 review, section 2 (3)), writes dK and dV (fp32) once and
+ * adds dQ into dQacc (fp32, must hold zeros or a partial sum) with atomics.
+ * D must come from attn_bwd_preprocess with the same O and dO. */
+attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const void* dO,
+                          const float* LSE, const float* D, attn_dtype dt,
+                          int B, int H, int N, int d, float scale, int causal,
+                          float* dQacc, float* dK, float* dV, void* stream);
+
+/* Bytes of device workspace attn_bwd needs: D (B*H*N fp32) rounded up to
+ * 256 bytes, plus the fp32 dQ accumulator (B*H*N*d fp32) when grad_dt is
+ * ATTN_BF16.  Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype grad_dt);
+
+/* Full backward = attn_bwd_preprocess + attn_bwd_main (+ a conversion of the
+ * fp32 accumulators to bf16 when grad_dt = ATTN_BF16).  Q, K, V, O, dO: dtype
+ * `dt`; LSE from attn_fwd with the same scale and causal flag.  dQ, dK, dV:
+ * outputs of dtype grad_dt.  workspace: device, 16-byte aligned, at least
+ * attn_bwd_workspace_bytes(B, H, N, d, grad_dt) bytes (else ATTN_EINVAL). */
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                     const void* dO, const float* LSE, attn_dtype dt,
+                     int B, int H, int N, int d, float scale, int causal,
+                     void* dQ, void* dK, void* dV, attn_dtype grad_dt,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* attn_status_str(attn_status s);
+
+/* hipError_t behind the calling thread's last ATTN_EHIP (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,90 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+Every request below fails validation, which the library performs before its
+first HIP call; the pointers are never dereferenced.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_12_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p(0x10000)          # non-null, 16-byte aligned, never touched
+MIS = ctypes.c_void_p(0x10008)        # misaligned
+NUL = ctypes.c_void_p(0)
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "attn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:attn_status|size_t|const char\*|int)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert set(_declared_functions()) == set(attn.EXPORTED)
+
+
+@pytest.mark.parametrize("name", _declared_functions())
+def test_library_exports_symbol(name):
+    assert hasattr(attn.lib(), name)
+
+
+def fwd(*, dt=1, B=1, H=1, N=16, d=64, scale=0.125, causal=0, q=P, o=P, lse=P):
+    return attn.lib().attn_fwd(q, P, P, dt, B, H, N, d, scale, causal, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=96), attn.ATTN_EUNSUPPORTED),
+    (dict(d=32), attn.ATTN_EUNSUPPORTED),
+    (dict(d=0), attn.ATTN_EINVAL),
+    (dict(N=0), attn.ATTN_EINVAL),
+    (dict(B=0), attn.ATTN_EINVAL),
+    (dict(H=-1), attn.ATTN_EINVAL),
+    (dict(dt=2), attn.ATTN_EINVAL),
+    (dict(scale=math.nan), attn.ATTN_EINVAL),
+    (dict(scale=math.inf), attn.ATTN_EINVAL),
+    (dict(causal=2), attn.ATTN_EINVAL),
+    (dict(q=NUL), attn.ATTN_EINVAL),
+    (dict(q=MIS), attn.ATTN_EINVAL),
+    (dict(o=NUL), attn.ATTN_EINVAL),
+    (dict(lse=MIS), attn.ATTN_EINVAL),
+    (dict(B=64, H=64, N=4096, d=128), attn.ATTN_EINVAL),       # B*H*N*d >= 2^31
+])
+def test_fwd_rejects_before_launch(kw, expect):
+    assert fwd(**kw) == expect
+
+
+def test_bwd_rejects_before_launch():
+    L = attn.lib()
+    ws = L.attn_bwd_workspace_bytes(1, 1, 16, 64, attn.ATTN_F32)
+    assert ws == 256
+    args = lambda d=64, wsb=ws, g=attn.ATTN_F32, w=P: (P, P, P, P, P, P, attn.ATTN_BF16, 1, 1, 16, d, 0.125, 1,
+                                                      P, P, P, g, w, ctypes.c_size_t(wsb), None)
+    assert L.attn_bwd(*args(wsb=ws - 1)) == attn.ATTN_EINVAL
+    assert L.attn_bwd(*args(d=100)) == attn.ATTN_EUNSUPPORTED
+    assert L.attn_bwd(*args(g=5)) == attn.ATTN_EINVAL
+    assert L.attn_bwd(*args(w=NUL)) == attn.ATTN_EINVAL
+    assert L.attn_bwd_main(P, P, P, P, P, P, 1, 1, 1, 16, 64, math.nan, 0, P, P, P, None) == attn.ATTN_EINVAL
+    assert L.attn_bwd_preprocess(P, MIS, 1, 1, 1, 16, 64, P, P, None) == attn.ATTN_EINVAL
+
+
+def test_workspace_sizes():
+    L = attn.lib()
+    rows = 4 * 16 * 4096
+    f32 = L.attn_bwd_workspace_bytes(4, 16, 4096, 128, attn.ATTN_F32)
+    bf = L.attn_bwd_workspace_bytes(4, 16, 4096, 128, attn.ATTN_BF16)
+    assert f32 == rows * 4
+    assert bf == rows * 4 + rows * 128 * 4
+    assert L.attn_bwd_workspace_bytes(0, 16, 4096, 128, attn.ATTN_F32) == 0
+
+
+def test_status_strings():
+    L = attn.lib()
+    for s in range(4):
+        assert L.attn_status_str(s)
+    assert L.attn_status_str(99) == b"unknown status"
+    assert L.attn_last_hip_error() == 0

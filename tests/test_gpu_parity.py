@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max-abs error <= 1e-5 for fp32 inputs and <= 2e-2 for bf16 inputs on
+O, LSE, dQ, dK and dV; the oracle receives the exact (bf16-rounded) inputs.
+Small shapes are compared element by element everywhere; the five workloads
+run at full size in the launch configuration the benchmark times, with the
+oracle evaluating sampled heads (in full) or sampled rows and key columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_tiled_attention_12_amd import attn_bwd, attn_fwd
+from exact_tiled_attention_12_amd.configs import CONFIGS
+from exact_tiled_attention_12_amd.inputs import config_inputs, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "bf16": 2e-2}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _err(gpu, ref):
+    return float(np.abs(gpu.detach().float().cpu().numpy() - ref).max())
+
+
+def _run(q, k, v, do, causal, scale=None, grad_dtype=torch.float32):
+    dev = _dev()
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = attn_fwd(qg, kg, vg, scale=scale, causal=causal)
+    grads = None
+    if do is not None:
+        grads = attn_bwd(qg, kg, vg, o, do.to(dev), lse, scale=scale, causal=causal, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return o, lse, grads
+
+
+def _check_full(q, k, v, do, causal, dtype, scale=None, tol=None, grad_dtype=torch.float32, relative=False):
+    """Element-wise comparison of every output.  relative=True (used only off the workloads,
+    where gradients can exceed the workloads' magnitude of about 4) scales the bar by
+    max(1, max|ref| / 4): bf16 rounding of P and dS is relative to the values."""
+    tol = TOL[dtype] if tol is None else tol
+    o, lse, grads = _run(q, k, v, do, causal, scale, grad_dtype)
+    O_ref, L_ref = oracle.fwd(q, k, v, scale=scale, causal=causal)
+    errs = {"O": (_err(o, O_ref), O_ref), "LSE": (_err(lse, L_ref), None)}
+    if do is not None:
+        dQ, dK, dV = oracle.bwd(q, k, v, do, scale=scale, causal=causal)
+        errs.update(dQ=(_err(grads[0], dQ), dQ), dK=(_err(grads[1], dK), dK), dV=(_err(grads[2], dV), dV))
+    _say("  max-abs errors:", {n: f"{e:.2e}" for n, (e, _) in errs.items()})
+    for n, (e, ref) in errs.items():
+        bar = tol
+        if relative and ref is not None:
+            bar = tol * max(1.0, float(np.abs(ref).max()) / 4.0)
+        assert e <= bar, f"{n}: {e} > {bar}"
+    return o, lse, grads
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 3, 17, 64, 130, 257])
+def test_small_shapes(dtype, d, causal, N):
+    _say(f"case small dtype={dtype} d={d} causal={causal} N={N}")
+    q, k, v, do = make_inputs(1, 2, N, d, dtype, seed=N * 1000 + d + causal)
+    _check_full(q, k, v, do, causal, dtype)
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_multi_tile(d, causal):
+    """Several 256-row blocks and 128-key blocks with a ragged tail, grid >= 256 workgroups."""
+    N = 1000
+    _say(f"case ragged d={d} causal={causal} N={N}")
+    q, k, v, do = make_inputs(2, 33, N, d, "bf16", seed=77 + d)
+    dev = _dev()
+    o, lse, (dq, dk, dv) = _run(q, k, v, do, causal)
+    for hh in (0, 65):        # first and last head
+        b, h = divmod(hh, 33)
+        O_ref, L_ref = oracle.fwd(q[b, h], k[b, h], v[b, h], causal=causal)
+        dQ, dK, dV = oracle.bwd(q[b, h], k[b, h], v[b, h], do[b, h], causal=causal)
+        errs = [_err(o[b, h], O_ref), _err(lse[b, h], L_ref), _err(dq[b, h], dQ), _err(dk[b, h], dK),
+                _err(dv[b, h], dV)]
+        _say("  head", hh, [f"{e:.2e}" for e in errs])
+        assert max(errs) <= TOL["bf16"]
+    assert dev.type == "cuda"
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.3])
+def test_scale_edge_values(scale):
+    """scale = 0 (uniform weights), a negative scale and a large one."""
+    _say(f"case scale={scale}")
+    q, k, v, do = make_inputs(1, 3, 150, 64, "bf16", seed=5)
+    _check_full(q, k, v, do, True, "bf16", scale=scale, relative=True)
+    _check_full(q, k, v, do, False, "bf16", scale=scale, relative=True)
+
+
+def test_bf16_gradients_option():
+    _say("case bf16 grads")
+    q, k, v, do = make_inputs(1, 2, 300, 128, "bf16", seed=9)
+    _check_full(q, k, v, do, True, "bf16", grad_dtype=torch.bfloat16)
+
+
+def test_forward_deterministic_and_overwrites_nan_poison():
+    _say("case determinism / NaN poison")
+    dev = _dev()
+    q, k, v, _ = make_inputs(2, 4, 777, 128, "bf16", seed=3, with_grad=False)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    o1 = torch.full_like(qg, float("nan"))
+    l1 = torch.full(qg.shape[:-1], float("nan"), device=dev)
+    attn_fwd(qg, kg, vg, causal=True, out=o1, lse=l1)
+    o2, l2 = attn_fwd(qg, kg, vg, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1.float()).all() and torch.isfinite(l1).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_backward_overwrites_nan_poison():
+    _say("case bwd NaN poison")
+    dev = _dev()
+    q, k, v, do = make_inputs(1, 3, 333, 80, "bf16", seed=4)
+    qg, kg, vg, dg = (t.to(dev) for t in (q, k, v, do))
+    o, lse = attn_fwd(qg, kg, vg, causal=True)
+    dq, dk, dv = (torch.full(q.shape, float("nan"), device=dev) for _ in range(3))
+    attn_bwd(qg, kg, vg, o, dg, lse, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size.
+# ---------------------------------------------------------------------------
+def _heads_to_check(BH):
+    return sorted({0, BH // 2 + 1, BH - 1})
+
+
+@pytest.mark.parametrize("idx", [1, 2, 5, 3])
+def test_workload_full_size(idx):
+    cfg = CONFIGS[idx]
+    _say(f"case workload {idx}: {cfg.name}")
+    q, k, v, do = config_inputs(cfg)
+    o, lse, grads = _run(q, k, v, do, cfg.causal)
+    BH = cfg.B * cfg.H
+    tol = TOL[cfg.dtype]
+    flat = lambda t: t.reshape(BH, cfg.N, cfg.d)
+    heads = list(range(BH)) if BH <= 2 else _heads_to_check(BH)[: 2 if cfg.N >= 4096 else 3]
+    for hh in heads:
+        qh, kh, vh = flat(q)[hh], flat(k)[hh], flat(v)[hh]
+        O_ref, L_ref = oracle.fwd(qh, kh, vh, causal=cfg.causal)
+        errs = {"O": _err(o.reshape(BH, cfg.N, cfg.d)[hh], O_ref), "LSE": _err(lse.reshape(BH, cfg.N)[hh], L_ref)}
+        if grads is not None:
+            dQ, dK, dV = oracle.bwd(qh, kh, vh, flat(do)[hh], causal=cfg.causal)
+            for n, g, r in zip(("dQ", "dK", "dV"), grads, (dQ, dK, dV)):
+                errs[n] = _err(g.reshape(BH, cfg.N, cfg.d)[hh], r)
+        _say(f"  head {hh}:", {n: f"{e:.2e}" for n, e in errs.items()})
+        for n, e in errs.items():
+            assert e <= tol, f"head {hh} {n}: {e} > {tol}"
+
+
+def test_workload_4_sampled():
+    """N = 16384: the oracle evaluates sampled query rows (O, LSE, dQ) and key rows (dK, dV)."""
+    cfg = CONFIGS[4]
+    _say(f"case workload 4 sampled: {cfg.name}")
+    q, k, v, do = config_inputs(cfg)
+    o, lse, (dq, dk, dv) = _run(q, k, v, do, cfg.causal)
+    rng = np.random.default_rng(4)
+    for hh in (0, cfg.H - 1):
+        rows = np.unique(np.concatenate([[0, 1, 255, 256, 8191, cfg.N - 1], rng.integers(0, cfg.N, 26)]))
+        Or, Lr, dQr = oracle.rows(q[0, hh], k[0, hh], v[0, hh], do[0, hh], rows, causal=True)
+        dKc, dVc = oracle.cols(q[0, hh], k[0, hh], v[0, hh], do[0, hh], rows, causal=True)
+        ridx = torch.as_tensor(rows)
+        errs = {"O": _err(o[0, hh][ridx], Or), "LSE": _err(lse[0, hh][ridx], Lr), "dQ": _err(dq[0, hh][ridx], dQr),
+                "dK": _err(dk[0, hh][ridx], dKc), "dV": _err(dv[0, hh][ridx], dVc)}
+        _say(f"  head {hh}:", {n: f"{e:.2e}" for n, e in errs.items()})
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], f"head {hh} {n}: {e}"
