@@ -1,0 +1,235 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = forward (attn_fwd) + backward preprocess (attn_bwd_preprocess) +
+backward main pass (attn_bwd_main) over one batch of resident synthetic
+inputs: the whole path, fwd and bwd.  Default workload: B=4, H=16, N=4096,
+d=128, causal, bf16 (the N = 4k case of the headline metric); the N = 16k case
+(B=1, H=16) is measured in the same run and reported under "secondary".
+
+Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s (4 N^2 d per head forward,
+2.5x that backward, halved for the causal mask) from the wall clock around
+the timed steps; per-kernel durations come from HIP events recorded on the
+stream the kernels run on; `roofline` is for the dominant kernel.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from exact_tiled_attention_12_amd import attn_bwd_main, attn_bwd_preprocess, attn_fwd  # noqa: E402
+from exact_tiled_attention_12_amd.configs import CONFIGS  # noqa: E402
+from exact_tiled_attention_12_amd.flops import attn_flops  # noqa: E402
+from exact_tiled_attention_12_amd.inputs import config_inputs  # noqa: E402
+
+METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=4k/16k, d=128"
+PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
+KERNEL_SOURCES = ["exact_tiled_attention_12_amd/csrc/attn_fwd.hip",
+                  "exact_tiled_attention_12_amd/csrc/attn_bwd.hip",
+                  "exact_tiled_attention_12_amd/csrc/attn_common.h"]
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    def __init__(self, cfg, dev):
+        self.cfg = cfg
+        q, k, v, do = config_inputs(cfg)
+        self.q, self.k, self.v, self.do = (t.to(dev) for t in (q, k, v, do))
+        B, H, N, d = q.shape
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        self.D = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        self.dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+        self.dk = torch.empty_like(self.dq)
+        self.dv = torch.empty_like(self.dq)
+        self.fl_fwd = attn_flops(B, H, N, d, cfg.causal, "fwd")
+        self.fl_bwd = attn_flops(B, H, N, d, cfg.causal, "bwd")
+
+    def step(self, ev=None):
+        c = self.cfg
+        if ev is not None:
+            ev[0].record()
+        attn_fwd(self.q, self.k, self.v, causal=c.causal, out=self.o, lse=self.lse)
+        if ev is not None:
+            ev[1].record()
+        attn_bwd_preprocess(self.o, self.do, D=self.D, dq_acc=self.dq)
+        if ev is not None:
+            ev[2].record()
+        attn_bwd_main(self.q, self.k, self.v, self.do, self.lse, self.D, self.dq, causal=c.causal,
+                      dk=self.dk, dv=self.dv)
+        if ev is not None:
+            ev[3].record()
+
+    def measure(self, steps, warmup):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        # wall clock over exactly `steps` steps, synchronised on both sides
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        # per-kernel durations from events on the kernels' stream
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        for e in evs:
+            self.step(e)
+        torch.cuda.synchronize()
+        fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e-3
+        pre = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e-3
+        main = sum(e[2].elapsed_time(e[3]) for e in evs) / steps * 1e-3
+        return wall, fwd, pre, main
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The fp64 oracle (as it stands) on whole heads of the same workload, fwd + bwd."""
+    import oracle
+    q, k, v, do = config_inputs(cfg)
+    BH = cfg.B * cfg.H
+    flat = lambda t: t.reshape(BH, cfg.N, cfg.d)
+    done, t0 = 0, time.perf_counter()
+    while done < BH:
+        oracle.fwd(flat(q)[done], flat(k)[done], flat(v)[done], causal=cfg.causal)
+        oracle.bwd(flat(q)[done], flat(k)[done], flat(v)[done], flat(do)[done], causal=cfg.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    fl = attn_flops(1, done, cfg.N, cfg.d, cfg.causal, "fwd+bwd")
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {BH} heads, naive fp64 forward + backward (explicit N x N S, P, dP, dS), "
+                      f"N={cfg.N}, d={cfg.d}, causal={cfg.causal}; {dt:.1f} s wall"}
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it matches these sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    ent = t.get("kernels", {}).get(kernel)
+    if not ent or t.get("source_hash") != source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-secondary", action="store_true", help="skip the N=16k measurement")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run a plain 1 GiB device copy (rocprofv3 counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "heads shard across GPUs with no exchange, but no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.copy_only:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel(), "launches": 3}))
+        return
+
+    cfg = CONFIGS[args.config]
+    log(f"bench: workload {cfg.index} ({cfg.name}), warmup {args.warmup}, steps {args.steps}")
+    w = Workload(cfg, dev)
+    wall, t_fwd, t_pre, t_main = w.measure(args.steps, args.warmup)
+    flops = w.fl_fwd + (w.fl_bwd if cfg.backward else 0.0)
+    value = flops / wall / 1e12
+    fwd_tf = w.fl_fwd / t_fwd / 1e12
+    bwd_tf = w.fl_bwd / (t_pre + t_main) / 1e12
+    main_tf = w.fl_bwd / t_main / 1e12
+    log(f"bench: step {wall * 1e3:.3f} ms; fwd {t_fwd * 1e6:.1f} us ({fwd_tf:.1f} TFLOP/s), "
+        f"bwd_pre {t_pre * 1e6:.1f} us, bwd_main {t_main * 1e6:.1f} us ({main_tf:.1f} TFLOP/s)")
+    B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+
+    # dominant kernel = the one with the largest share of the step
+    kern = {"attn_bwd_main": (t_main, w.fl_bwd), "attn_fwd": (t_fwd, w.fl_fwd)}
+    dom = max(kern, key=lambda n: kern[n][0])
+    t_dom, fl_dom = kern[dom]
+    achieved = fl_dom / t_dom / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_flop_per_launch": fl_dom, "avg_launch_us": round(t_dom * 1e6, 2),
+                "traffic": load_traffic(dom)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"attention fwd+bwd, B={B} H={H} N={N} d={d} causal={cfg.causal} bf16 "
+                               f"(Q,K,V,dO ~ N(0,1), seed {cfg.seed})",
+                   "global_batch": B, "seq_len": N, "heads": H, "head_dim": d, "causal": cfg.causal,
+                   "parallelism": "single GPU"},
+        "kernels": {
+            "attn_fwd": {"us": round(t_fwd * 1e6, 2), "tflops": round(fwd_tf, 2),
+                         "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+            "attn_bwd_preprocess": {"us": round(t_pre * 1e6, 2)},
+            "attn_bwd_main": {"us": round(t_main * 1e6, 2), "tflops": round(main_tf, 2),
+                              "frac_peak": round(main_tf / PEAK_BF16_TFLOPS, 4)},
+            "bwd_total_tflops": round(bwd_tf, 2), "bwd_frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+        },
+        "roofline": roofline,
+        "source_hash": source_hash(),
+    }
+
+    if cfg.index == 3 and not args.no_secondary:
+        cfg4 = CONFIGS[4]
+        del w
+        torch.cuda.empty_cache()
+        log("bench: secondary workload 4 (N=16384)")
+        w4 = Workload(cfg4, dev)
+        steps4 = max(3, args.steps // 2)
+        wall4, f4, p4, m4 = w4.measure(steps4, max(2, args.warmup // 2))
+        out["secondary"] = {
+            "workload": f"B=1 H=16 N=16384 d=128 causal bf16 (Q,K x0.5)", "steps": steps4,
+            "ms_per_step": round(wall4 * 1e3, 4),
+            "value": round((w4.fl_fwd + w4.fl_bwd) / wall4 / 1e12, 2),
+            "fwd_tflops": round(w4.fl_fwd / f4 / 1e12, 2),
+            "fwd_frac_peak": round(w4.fl_fwd / f4 / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_tflops": round(w4.fl_bwd / (p4 + m4) / 1e12, 2),
+            "bwd_frac_peak": round(w4.fl_bwd / (p4 + m4) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        }
+        log(f"bench: N=16384 step {wall4 * 1e3:.3f} ms")
+
+    if not args.no_cpu:
+        log("bench: CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -58,10 +58,41 @@ __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes
+// return zeros (hardware range check), which is how rows past N read as 0.
+// Word 3 = 0x00020000: 32-bit data format, as untyped buffer loads require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// max(a, b, c) in one v_max3_f32.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 // Lane with the same query in the other half of the wave.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Largest p the forward lets a probability reach before it moves its reference
+// max: 2^8 (log2 units).  Keeps fp32 sums and bf16 probabilities far from overflow.
+constexpr float kLazyLog2 = 8.0f;
+
+// Sum of the two bf16 halves of x added to acc (v_dot2_f32_bf16 against ones).
+__device__ __forceinline__ float sum2_bf16(uint32_t x, float acc)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(bf16)1.0f, (bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), ones, acc, false);
+}
 
 // Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }

@@ -57,16 +57,17 @@ struct FwdCfg {
     static_assert(SMEM_ELEMS * sizeof(T) <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int D, bool CAUSAL, int QT>
-__global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                  const T* __restrict__ V, T* __restrict__ O,
-                                                  float* __restrict__ LSE, int N, int nqblk, float c,
-                                                  int negate_q)
+template <typename T, int D, bool CAUSAL, int QT, int MINW>
+__global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                        const T* __restrict__ V, T* __restrict__ O,
+                                                        float* __restrict__ LSE, int N, int nqblk, float c,
+                                                        int negate_q)
 {
     using C = FwdCfg<T, D, QT>;
     using M = Mma<T>;
     typedef typename M::frag frag;
     constexpr float NEG_INF = -__builtin_inff();
+    constexpr bool BF = sizeof(T) == 2;
 
     __shared__ __attribute__((aligned(16))) T smem[C::SMEM_ELEMS];
 
@@ -80,24 +81,28 @@ __global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const
     const int q0 = qb * C::BM;
     const int q0w = q0 + wave * 32 * QT;             // this wave's first query row
     const size_t hoff = (size_t)head * (size_t)N * D;
-    const T* __restrict__ Qh = Q + hoff;
     const T* __restrict__ Kh = K + hoff;
     const T* __restrict__ Vh = V + hoff;
+    constexpr uint32_t ROWB = D * sizeof(T);         // bytes per row
 
     // ---- Q fragments (B operand of S^T = K Q^T), held for the whole pass ----
     frag qf[QT][C::NKS];
+    {
+        const auto rq = make_rsrc(Q + hoff, (uint32_t)N * ROWB);
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-        const int q = q0w + 32 * t + l32;
+        for (int t = 0; t < QT; ++t) {
+            const uint32_t rowoff = (uint32_t)(q0w + 32 * t + l32) * ROWB;
 #pragma unroll
-        for (int s = 0; s < C::NKS; ++s) {
-            if constexpr (sizeof(T) == 2) {
-                u32x4 raw = q < N ? ld16(Qh + (size_t)q * D + s * C::KS + C::E * h) : zero4();
-                if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-                qf[t][s] = __builtin_bit_cast(bf16x8, raw);
-            } else {
-                float x = q < N ? Qh[(size_t)q * D + s * C::KS + h] : 0.f;
-                qf[t][s] = negate_q ? -x : x;
+            for (int s = 0; s < C::NKS; ++s) {
+                const uint32_t off = rowoff + (s * C::KS + C::E * h) * sizeof(T);
+                if constexpr (BF) {
+                    u32x4 raw = buf_ld16(rq, off);
+                    if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+                    qf[t][s] = __builtin_bit_cast(bf16x8, raw);
+                } else {
+                    const float x = buf_ld4f(rq, off);
+                    qf[t][s] = negate_q ? -x : x;
+                }
             }
         }
     }
@@ -118,57 +123,58 @@ __global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const
         for (int t = 0; t < QT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[dt][t][r] = 0.f;
-    float m[QT], l[QT];
+    float mc[QT], l[QT];
 #pragma unroll
-    for (int t = 0; t < QT; ++t) { m[t] = NEG_INF; l[t] = 0.f; }
+    for (int t = 0; t < QT; ++t) { mc[t] = NEG_INF; l[t] = 0.f; }
 
     const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
     const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
-    // ---- staging: global -> registers -> LDS ----
+    // ---- staging: global -> registers -> LDS (per-thread offsets are loop invariant) ----
+    uint32_t koff[C::KLD], voff[C::VLD];
+    int kst_row[C::KLD], kst_col[C::KLD], vst_g[C::VLD], vst_col[C::VLD];
+#pragma unroll
+    for (int i = 0; i < C::KLD; ++i) {
+        const int f = tid + C::THREADS * i;
+        kst_row[i] = f / C::CPR;
+        kst_col[i] = f - kst_row[i] * C::CPR;
+        koff[i] = kst_row[i] * ROWB + kst_col[i] * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VLD; ++i) {
+        const int f = tid + C::THREADS * i;
+        vst_g[i] = f / C::CPR;
+        vst_col[i] = f - vst_g[i] * C::CPR;
+        voff[i] = 4 * vst_g[i] * ROWB + vst_col[i] * 16;
+    }
     u32x4 kst[C::KLD];
     u32x4 vst[C::VLD][4];
     auto load_tile = [&](int j) {
         const int kv0 = j * C::BN;
+        const uint32_t bytes = (uint32_t)(N - kv0) * ROWB;        // rows past N read as zeros
+        const auto rk = make_rsrc(Kh + (size_t)kv0 * D, bytes);
+        const auto rv = make_rsrc(Vh + (size_t)kv0 * D, bytes);
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int f = tid + C::THREADS * i;
-            if (f < C::KCHUNKS) {
-                const int row = f / C::CPR, col = f - row * C::CPR;
-                const int key = kv0 + row;
-                kst[i] = key < N ? ld16(Kh + (size_t)key * D + col * C::CH) : zero4();
+        for (int i = 0; i < C::KLD; ++i)
+            if (C::KCHUNKS % C::THREADS == 0 || tid + C::THREADS * i < C::KCHUNKS) kst[i] = buf_ld16(rk, koff[i]);
+#pragma unroll
+        for (int i = 0; i < C::VLD; ++i)
+            if (C::VGROUPS % C::THREADS == 0 || tid + C::THREADS * i < C::VGROUPS) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vst[i][e] = buf_ld16(rv, voff[i] + e * ROWB);
             }
-        }
-#pragma unroll
-        for (int i = 0; i < C::VLD; ++i) {
-            const int f = tid + C::THREADS * i;
-            if (f < C::VGROUPS) {
-                const int g = f / C::CPR, col = f - g * C::CPR;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = kv0 + 4 * g + e;
-                    vst[i][e] = key < N ? ld16(Vh + (size_t)key * D + col * C::CH) : zero4();
-                }
-            }
-        }
     };
-    auto store_tile = [&](int buf) {
-        T* Kl = smem + buf * (C::KBUF + C::VBUF);
+    auto store_tile = [&](T* Kl) {
         T* Vl = Kl + C::KBUF;
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int f = tid + C::THREADS * i;
-            if (f < C::KCHUNKS) {
-                const int row = f / C::CPR, col = f - row * C::CPR;
-                st16(Kl + row * C::KPITCH + col * C::CH, kst[i]);
-            }
-        }
+        for (int i = 0; i < C::KLD; ++i)
+            if (C::KCHUNKS % C::THREADS == 0 || tid + C::THREADS * i < C::KCHUNKS)
+                st16(Kl + kst_row[i] * C::KPITCH + kst_col[i] * C::CH, kst[i]);
 #pragma unroll
-        for (int i = 0; i < C::VLD; ++i) {
-            const int f = tid + C::THREADS * i;
-            if (f < C::VGROUPS) {
-                const int g = f / C::CPR, col = f - g * C::CPR;
-                if constexpr (sizeof(T) == 2) {
+        for (int i = 0; i < C::VLD; ++i)
+            if (C::VGROUPS % C::THREADS == 0 || tid + C::THREADS * i < C::VGROUPS) {
+                const int g = vst_g[i], col = vst_col[i];
+                if constexpr (BF) {
                     // 4 keys x 8 head-dim values -> for each of the 8 dims, 4 keys (8 bytes).
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
@@ -189,23 +195,11 @@ __global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const
                     }
                 }
             }
-        }
     };
 
-    load_tile(0);
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        store_tile(buf);
-        __syncthreads();
-        if (j + 1 < ntiles) load_tile(j + 1);
-
-        const int kv0 = j * C::BN;
-        if (CAUSAL && kv0 > q0w + 32 * QT - 1) continue;     // every key is above this wave's rows
-
-        const T* Kl = smem + buf * (C::KBUF + C::VBUF);
+    // ---- one key tile: S^T, online softmax, O^T += V^T P^T ----
+    auto compute_tile = [&](const T* Kl, int kv0) {
         const T* Vl = Kl + C::KBUF;
-
-        // ---- S^T = K Q^T (raw dot products; the scale is folded into the exponent) ----
         f32x16 sacc[C::NKT][QT];
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
@@ -219,90 +213,105 @@ __global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const
             for (int kt = 0; kt < C::NKT; ++kt) {
                 const T* src = Kl + (32 * kt + l32) * C::KPITCH + s * C::KS + C::E * h;
                 frag a;
-                if constexpr (sizeof(T) == 2) a = __builtin_bit_cast(bf16x8, ld16(src));
+                if constexpr (BF) a = __builtin_bit_cast(bf16x8, ld16(src));
                 else a = *src;
 #pragma unroll
                 for (int t = 0; t < QT; ++t) sacc[kt][t] = M::mma(a, qf[t][s], sacc[kt][t]);
             }
         }
 
-        // ---- online softmax (per lane: one query, 16 keys per sub-tile) ----
+        // mc[t] is the reference max in log2 units (max * scale * log2 e).  It only
+        // moves when the tile's max exceeds it by more than kLazyLog2 (so every p
+        // stays <= 2^kLazyLog2): most tiles then need no rescale of O and l at all.
         const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > q0w) || (kv0 + C::BN > N);
+        frag pf[C::NKT][32 / C::KS][QT];
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
-            const int q = q0w + 32 * t + l32;
-            float mx = NEG_INF;
             if (need_mask) {
+                const int q = q0w + 32 * t + l32;
 #pragma unroll
                 for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const bool dead = (CAUSAL && key > q) || key >= N;
-                        if (dead) sacc[kt][t][r] = NEG_INF;
-                        mx = fmaxf(mx, sacc[kt][t][r]);
+                        if ((CAUSAL && key > q) || key >= N) sacc[kt][t][r] = NEG_INF;
                     }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][t][r]);
             }
+            float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2)
+                    mx4[r >> 2] = max3f(mx4[r >> 2], sacc[kt][t][r], sacc[kt][t][r + 1]);
+            float mx = max3f(mx4[0], mx4[1], fmaxf(mx4[2], mx4[3]));
             mx = fmaxf(mx, xor32(mx));
-            const float mnew = fmaxf(m[t], mx);
-            const float ms = (mnew == NEG_INF) ? 0.f : mnew * c;
-            const float alpha = (m[t] == NEG_INF) ? 0.f : fast_exp2(fmaf(m[t], c, -ms));
-            float rs = 0.f;
+            const float mxc = (mx == NEG_INF) ? NEG_INF : mx * c;
+            if (__builtin_amdgcn_ballot_w64(mxc > mc[t] + kLazyLog2) != 0) {
+                const float mnew = fmaxf(mc[t], mxc);
+                const float alpha = fast_exp2(mc[t] - mnew);       // 0 on the first tile
+                l[t] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][t][r] *= alpha;
+                mc[t] = mnew;
+            }
+            const float ms = mc[t];
             if (need_mask) {
 #pragma unroll
                 for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float sv = sacc[kt][t][r];
-                        const float p = (sv == NEG_INF) ? 0.f : fast_exp2(fmaf(sv, c, -ms));
-                        sacc[kt][t][r] = p;
-                        rs += p;
+                        sacc[kt][t][r] = (sv == NEG_INF) ? 0.f : fast_exp2(fmaf(sv, c, -ms));
                     }
             } else {
 #pragma unroll
                 for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = fast_exp2(fmaf(sacc[kt][t][r], c, -ms));
-                        sacc[kt][t][r] = p;
-                        rs += p;
-                    }
+                    for (int r = 0; r < 16; ++r) sacc[kt][t][r] = fast_exp2(fmaf(sacc[kt][t][r], c, -ms));
             }
-            l[t] = fmaf(l[t], alpha, rs);
-            m[t] = mnew;
+            // P in the MFMA operand type; the row sum is taken over exactly these values.
+            if constexpr (BF) {
+                float ls[2] = {0.f, 0.f};
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
+                for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[dt][t][r] *= alpha;
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        bf16x8 pb;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) pb[e] = to_bf16(sacc[kt][t][8 * s2 + e]);
+                        const u32x4 w = __builtin_bit_cast(u32x4, pb);
+                        ls[s2] = sum2_bf16(w[0], ls[s2]);
+                        ls[s2] = sum2_bf16(w[1], ls[s2]);
+                        ls[s2] = sum2_bf16(w[2], ls[s2]);
+                        ls[s2] = sum2_bf16(w[3], ls[s2]);
+                        pf[kt][s2][t] = pb;
+                    }
+                l[t] += ls[0] + ls[1];
+            } else {
+                float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        pf[kt][r][t] = sacc[kt][t][r];
+                        ls[r & 3] += sacc[kt][t][r];
+                    }
+                l[t] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            }
         }
 
-        // ---- O^T += V^T P^T ----
+        // O^T += V^T P^T
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt) {
 #pragma unroll
             for (int s2 = 0; s2 < 32 / C::KS; ++s2) {
-                frag b[QT];
-#pragma unroll
-                for (int t = 0; t < QT; ++t) {
-                    if constexpr (sizeof(T) == 2) {
-                        bf16x8 pb;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) pb[e] = to_bf16(sacc[kt][t][8 * s2 + e]);
-                        b[t] = pb;
-                    } else {
-                        b[t] = sacc[kt][t][s2];
-                    }
-                }
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt) {
                     const T* vrow = Vl + (32 * dt + l32) * C::VPITCH + 32 * kt;
                     frag a;
-                    if constexpr (sizeof(T) == 2) {
+                    if constexpr (BF) {
                         const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 4 * h);
                         const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 8 + 4 * h);
                         a = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
@@ -310,10 +319,25 @@ __global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const
                         a = vrow[8 * (s2 >> 2) + 4 * h + (s2 & 3)];
                     }
 #pragma unroll
-                    for (int t = 0; t < QT; ++t) oacc[dt][t] = M::mma(a, b[t], oacc[dt][t]);
+                    for (int t = 0; t < QT; ++t) oacc[dt][t] = M::mma(a, pf[kt][s2][t], oacc[dt][t]);
                 }
             }
         }
+    };
+
+    // ---- main loop, unrolled by two so the LDS buffer offsets are constants ----
+    auto step = [&](int j, T* Kl) {
+        store_tile(Kl);
+        __syncthreads();
+        if (j + 1 < ntiles) load_tile(j + 1);
+        const int kv0 = j * C::BN;
+        if (!(CAUSAL && kv0 > q0w + 32 * QT - 1))        // else: every key is above this wave's rows
+            compute_tile(Kl, kv0);
+    };
+    load_tile(0);
+    for (int j = 0; j < ntiles; j += 2) {
+        step(j, smem);
+        if (j + 1 < ntiles) step(j + 1, smem + C::KBUF + C::VBUF);
     }
 
     // ---- epilogue: one division by l, O and LSE written once ----
@@ -331,7 +355,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const
                     const int d0 = 32 * dt + 8 * g + 4 * h;
                     if (d0 < D) {
                         T* dst = Oh + (size_t)q * D + d0;
-                        if constexpr (sizeof(T) == 2) {
+                        if constexpr (BF) {
                             bf16x4 v;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) v[e] = to_bf16(oacc[dt][t][4 * g + e] * inv);
@@ -344,12 +368,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(const T* __restrict__ Q, const
                         }
                     }
                 }
-            if (h == 0) LSE[(size_t)head * N + q] = (m[t] * c + __log2f(lt)) * kLn2;
+            if (h == 0) LSE[(size_t)head * N + q] = (mc[t] + __log2f(lt)) * kLn2;
         }
     }
 }
 
-template <typename T, int D, bool CAUSAL, int QT>
+template <typename T, int D, bool CAUSAL, int QT, int MINW>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int BH, int N, float scale, hipStream_t st)
 {
@@ -357,26 +381,31 @@ static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void
     const int nqblk = (N + C::BM - 1) / C::BM;
     const float c = fabsf(scale) * kLog2e;
     const int negq = scale < 0.f;
-    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, QT>), dim3(nqblk * BH), dim3(C::THREADS), 0, st,
+    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, QT, MINW>), dim3(nqblk * BH), dim3(C::THREADS), 0, st,
                        (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, nqblk, c, negq);
     return hipGetLastError();
 }
+
+// Tile table.  bf16: one 32-row query tile per wave and two workgroups per CU
+// (<= 256 registers per wave), so that one wave's softmax runs on the VALU
+// while the other wave of the same SIMD keeps the matrix cores busy.
+// fp32 (fragments four times larger per contraction step): one workgroup per CU.
+#ifndef ATTN_FWD_BF16_QT
+#define ATTN_FWD_BF16_QT 1
+#endif
+#ifndef ATTN_FWD_BF16_MINW
+#define ATTN_FWD_BF16_MINW 2
+#endif
 
 template <typename T, int D>
 static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int BH, int N, float scale, int causal, hipStream_t st)
 {
-    // Two query tiles per wave (BM = 256) halve the LDS reads per MFMA; use them
-    // when the grid still has enough workgroups to fill 256 CUs.
-    constexpr bool big_ok = sizeof(T) == 2;
-    const long wg_big = (long)BH * ((N + 255) / 256);
-    const bool big = big_ok && wg_big >= 256;
-    if (causal) {
-        if (big) return launch_fwd_t<T, D, true, big_ok ? 2 : 1>(Q, K, V, O, LSE, BH, N, scale, st);
-        return launch_fwd_t<T, D, true, 1>(Q, K, V, O, LSE, BH, N, scale, st);
-    }
-    if (big) return launch_fwd_t<T, D, false, big_ok ? 2 : 1>(Q, K, V, O, LSE, BH, N, scale, st);
-    return launch_fwd_t<T, D, false, 1>(Q, K, V, O, LSE, BH, N, scale, st);
+    constexpr bool isbf = sizeof(T) == 2;
+    constexpr int QT = isbf ? ATTN_FWD_BF16_QT : 1;
+    constexpr int MINW = isbf ? ATTN_FWD_BF16_MINW : 1;
+    if (causal) return launch_fwd_t<T, D, true, QT, MINW>(Q, K, V, O, LSE, BH, N, scale, st);
+    return launch_fwd_t<T, D, false, QT, MINW>(Q, K, V, O, LSE, BH, N, scale, st);
 }
 
 hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, bool bf16_in,

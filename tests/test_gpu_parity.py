@@ -46,9 +46,10 @@ def _run(q, k, v, do, causal, scale=None, grad_dtype=torch.float32):
 
 
 def _check_full(q, k, v, do, causal, dtype, scale=None, tol=None, grad_dtype=torch.float32, relative=False):
-    """Element-wise comparison of every output.  relative=True (used only off the workloads,
-    where gradients can exceed the workloads' magnitude of about 4) scales the bar by
-    max(1, max|ref| / 4): bf16 rounding of P and dS is relative to the values."""
+    """Element-wise comparison of every output.  relative=True (used only off the five
+    workloads, where a sharper softmax makes the gradients larger than the workloads'
+    magnitude of about 4) uses max(tol, 1% of max|ref|): the bf16 roundings of O (which D
+    is built from), P and dS are relative to the values."""
     tol = TOL[dtype] if tol is None else tol
     o, lse, grads = _run(q, k, v, do, causal, scale, grad_dtype)
     O_ref, L_ref = oracle.fwd(q, k, v, scale=scale, causal=causal)
@@ -60,7 +61,7 @@ def _check_full(q, k, v, do, causal, dtype, scale=None, tol=None, grad_dtype=tor
     for n, (e, ref) in errs.items():
         bar = tol
         if relative and ref is not None:
-            bar = tol * max(1.0, float(np.abs(ref).max()) / 4.0)
+            bar = max(tol, 1e-2 * float(np.abs(ref).max()))
         assert e <= bar, f"{n}: {e} > {bar}"
     return o, lse, grads
 
