@@ -18,6 +18,9 @@ attn_status check_shape(int B, int H, int N, int d)
     if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_EINVAL;
     const long long total = (long long)B * H * N * d;
     if (total >= (1LL << 31)) return ATTN_EINVAL;
+    // one head's fp32 rows must stay below 2 GiB: the kernels address a head
+    // with 32-bit byte offsets and use 2^31 as their out-of-range offset
+    if ((long long)N * d * 4 >= (1LL << 31)) return ATTN_EINVAL;
     if (d != 64 && d != 80 && d != 128) return ATTN_EUNSUPPORTED;
     return ATTN_OK;
 }

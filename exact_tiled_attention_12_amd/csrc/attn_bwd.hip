@@ -425,6 +425,260 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
     }
 }
 
+// ----------------------------------------------------------------------------
+// Main backward kernel, bf16 inputs (the hot path).
+//
+// LDS, every tile in swizzled rows and written by direct-to-LDS loads except dS^T:
+//   sQ0/sQ1, sG0/sG1 : Q and dO rows of the current / next query block (row reads
+//                      for S = Q K^T and dP = dO V^T, transpose reads for Q^T, dO^T)
+//   sK               : the workgroup's BN key rows (row reads: B operand of S;
+//                      transpose reads: B operand of dQ = dS K)
+//   sS0/sS1          : dS^T [key][query] of the current / previous block
+//   sL*, sD*         : -LSE*log2 e and D of the block's rows
+// Each buffer is its own __shared__ object and the loop is unrolled by two, so
+// the compiler can tell the in-flight direct-to-LDS loads (next block) from the
+// LDS reads of the current block and does not wait for them.  One barrier per
+// query block: the dQ product of block i-1 runs after the barrier of block i.
+// ----------------------------------------------------------------------------
+template <int D>
+struct BwdBf16Cfg {
+    static constexpr int BN = 128, BM = 64, NQT = BM / 32;
+    static constexpr int RB = D == 64 ? 128 : 256;        // LDS bytes per Q/dO/K row
+    static constexpr int DP = (D + 31) / 32 * 32, NDT = DP / 32;
+    static constexpr int NKS = D / 16;
+    static constexpr int SRB = BM * 2;                    // bytes per dS^T row (128)
+    static constexpr int Q_BYTES = BM * RB, K_BYTES = BN * RB, S_BYTES = BN * SRB;
+    static constexpr int DQ_PER_WAVE = (NDT + 1) / 2;     // dQ head-dim tiles per wave
+    static constexpr int BYTES = 4 * Q_BYTES + K_BYTES + 2 * S_BYTES + 4 * BM * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(SRB == 128, "dS^T rows use the 128-byte swizzle");
+};
+
+template <int D, bool CAUSAL, typename G>
+__global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                       const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                                                       const float* __restrict__ LSE, const float* __restrict__ Dg,
+                                                       float* __restrict__ dQacc, G* __restrict__ dK,
+                                                       G* __restrict__ dV, int N, int nkblk, float scale)
+{
+    using C = BwdBf16Cfg<D>;
+    constexpr int RB = C::RB;
+    constexpr uint32_t ROWB = D * 2;                    // global bytes per row
+    __shared__ __attribute__((aligned(1024))) char sQ0[C::Q_BYTES], sQ1[C::Q_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sG0[C::Q_BYTES], sG1[C::Q_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sK[C::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sS0[C::S_BYTES], sS1[C::S_BYTES];
+    __shared__ __attribute__((aligned(16))) float sL0[C::BM], sL1[C::BM], sD0[C::BM], sD1[C::BM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform (scalar branches)
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = bid / nkblk;
+    const int kb = bid - head * nkblk;
+    const int k0 = kb * C::BN;
+    const int k0w = k0 + 32 * wave;
+    const int mykey = k0w + l32;
+    const size_t hoff = (size_t)head * (size_t)N * D;
+    const bf16* __restrict__ Qh = Q + hoff;
+    const bf16* __restrict__ dOh = dO + hoff;
+    const uint32_t head_bytes = (uint32_t)N * ROWB;
+    const float c2 = scale * kLog2e;
+    TileLane<RB, C::NKS> tl;            // Q, dO, K tiles
+    TileLane<128, 1> ts;                // dS^T tiles
+    tl.init(lane);
+    ts.init(lane);
+
+    // ---- resident V fragments (B operand of dP = dO V^T) ----
+    bf16x8 vf[C::NKS];
+    {
+        const auto rv = make_rsrc(V + hoff, head_bytes);
+        const uint32_t ro = (uint32_t)mykey * ROWB + 16 * h;
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) vf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rv, ro + 32 * s));
+    }
+    // ---- the workgroup's K rows in LDS ----
+    dma_rows<D, RB>(make_rsrc(K + hoff + (size_t)k0 * D, (uint32_t)(N - k0) * ROWB), sK, wave * (C::BN / 4),
+                    C::BN / 4, lane);
+
+    f32x16 dvacc[C::NDT], dkacc[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dvacc[dt][r] = 0.f; dkacc[dt][r] = 0.f; }
+
+    const int nq = (N + C::BM - 1) / C::BM;
+    const int i0 = CAUSAL ? (k0 / C::BM) : 0;
+    const auto rdq = make_rsrc(dQacc + hoff, (uint32_t)N * D * 4);
+    // vector-memory instructions one dq phase issues on this wave (all atomics)
+    constexpr int dq_vm = 16 * C::DQ_PER_WAVE;
+
+    // Loads of query block i: Q and dO rows by DMA (16 rows per wave each);
+    // -LSE*log2e (wave 0) and D (wave 1) into a register, parked in LDS later.
+    float lreg = 0.f;
+    auto issue_block = [&](int i, char* sQ, char* sG) {
+        const int q0 = i * C::BM;
+        const uint32_t bytes = (uint32_t)(N - q0) * ROWB;
+        dma_rows<D, RB>(make_rsrc(Qh + (size_t)q0 * D, bytes), sQ, wave * (C::BM / 4), C::BM / 4, lane);
+        dma_rows<D, RB>(make_rsrc(dOh + (size_t)q0 * D, bytes), sG, wave * (C::BM / 4), C::BM / 4, lane);
+        if (wave == 0)
+            lreg = -kLog2e * buf_ld4f(make_rsrc(LSE + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
+        if (wave == 1) lreg = buf_ld4f(make_rsrc(Dg + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
+    };
+
+    // dQ[q][d] += scale * sum_key dS[q][key] K[key][d] for query block i from dS^T.
+    // Wave w: query tile w % 2, head-dim tiles w / 2 and w / 2 + 2.
+    auto dq_phase = [&](int i, const char* sS) {
+        const int qt = wave & 1;
+        f32x16 acc[C::DQ_PER_WAVE];
+#pragma unroll
+        for (int x = 0; x < C::DQ_PER_WAVE; ++x)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::BN / 16; ++s) {
+            const bf16x8 af = ts.tr(sS, 16 * s, qt);
+#pragma unroll
+            for (int x = 0; x < C::DQ_PER_WAVE; ++x)      // for d = 80, tile 3 reads zero columns
+                acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, tl.tr(sK, 16 * s, (wave >> 1) + 2 * x), acc[x], 0, 0, 0);
+        }
+#pragma unroll
+        for (int x = 0; x < C::DQ_PER_WAVE; ++x) {
+            const int dt = (wave >> 1) + 2 * x;
+            const int dcol = 32 * dt + l32;
+            if (dcol < D) {
+                const uint32_t base = (uint32_t)(i * C::BM + 32 * qt + 4 * h) * (D * 4) + dcol * 4;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[x][r] * scale, rdq,
+                                                                    (int)(base + (8 * (r >> 2) + (r & 3)) * (D * 4)), 0, 0);
+            }
+        }
+    };
+
+    // One query block: S, dP, P, dS, dS^T -> LDS, dV += dO^T P, dK += Q^T dS.
+    auto block_body = [&](int i, const char* sQ, const char* sG, char* sS, const float* sL, const float* sD) {
+        const int q0 = i * C::BM;
+        f32x16 sacc[C::NQT], pacc[C::NQT];
+#pragma unroll
+        for (int qt = 0; qt < C::NQT; ++qt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { sacc[qt][r] = 0.f; pacc[qt][r] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+            const bf16x8 kf = tl.row(sK + 32 * wave * RB, 0, s);
+#pragma unroll
+            for (int qt = 0; qt < C::NQT; ++qt) {
+                sacc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sQ, 32 * qt, s), kf, sacc[qt], 0, 0, 0);
+                pacc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sG, 32 * qt, s), vf[s], pacc[qt], 0, 0, 0);
+            }
+        }
+        // P = exp2(S c2 - LSE log2 e);  dS = P o (dP - D);  both to bf16
+        // (a wave whose keys all follow the block's queries gets P = 0 from the mask;
+        // skipping it instead would split the accumulators' live ranges)
+        const bool need_mask = CAUSAL && (q0 < k0w + 31);
+        bf16x8 pb[C::NQT][2], sb[C::NQT][2];
+#pragma unroll
+        for (int qt = 0; qt < C::NQT; ++qt) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int qo = 32 * qt + 8 * g4 + 4 * h;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + qo);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + qo);
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(sacc[qt][4 * g4 + e], c2, l4[e]));
+                if (need_mask) {              // diagonal blocks only: key > query -> 0
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (mykey > q0 + qo + e) p[e] = 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ds = p[e] * (pacc[qt][4 * g4 + e] - d4[e]);
+                    pb[qt][g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e]);
+                    sb[qt][g4 >> 1][4 * (g4 & 1) + e] = to_bf16(ds);
+                }
+            }
+        }
+        // dS^T -> LDS (rows = keys, 4 consecutive queries per 8-byte write)
+        {
+            const int row = 32 * wave + l32;
+#pragma unroll
+            for (int qt = 0; qt < C::NQT; ++qt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const u32x4 w = __builtin_bit_cast(u32x4, sb[qt][g4 >> 1]);
+                    const u32x2 v2 = (g4 & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+                    *reinterpret_cast<u32x2*>(sS + row * C::SRB + swz<128>(row, 4 * qt + g4) * 16 + 8 * h) = v2;
+                }
+        }
+        // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over the block's queries)
+#pragma unroll
+        for (int qt = 0; qt < C::NQT; ++qt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt) {
+                    const int k0q = 32 * qt + 16 * s2;
+                    dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sG, k0q, dt), pb[qt][s2], dvacc[dt], 0, 0, 0);
+                    dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sQ, k0q, dt), sb[qt][s2], dkacc[dt], 0, 0, 0);
+                }
+    };
+
+    // One step of the pipeline for block i with static buffers (cur = block i, nxt = block i+1).
+    auto step = [&](int i, char* qc, char* gc, char* sc, float* lc, float* dc, char* qn, char* gn, char* sn) {
+        // block i's Q/dO/stat loads are in flight since the previous step; the dQ atomics
+        // issued after them may stay in flight (vector memory completes in issue order)
+        if (i > i0 + 1) wait_vmem_leave(dq_vm);
+        else wait_vmem_all();
+        if (wave == 0) lc[lane] = lreg;
+        if (wave == 1) dc[lane] = lreg;
+        __syncthreads();
+        if (i + 1 < nq) issue_block(i + 1, qn, gn);
+        if (i > i0) dq_phase(i - 1, sn);                // dS^T of block i-1 lives in the other buffer
+        block_body(i, qc, gc, sc, lc, dc);
+    };
+
+    issue_block(i0, sQ0, sG0);
+    int i = i0;
+    for (; i + 1 < nq; i += 2) {
+        step(i, sQ0, sG0, sS0, sL0, sD0, sQ1, sG1, sS1);
+        step(i + 1, sQ1, sG1, sS1, sL1, sD1, sQ0, sG0, sS0);
+    }
+    if (i < nq) step(i, sQ0, sG0, sS0, sL0, sD0, sQ1, sG1, sS1);
+    __syncthreads();
+    dq_phase(nq - 1, ((nq - 1 - i0) & 1) ? sS1 : sS0);
+
+    // ---- dK = scale * dK^T acc, dV = dV^T acc, written once ----
+    if (mykey < N) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * dt + 8 * g4 + 4 * h;
+                if (d0 < D) {
+                    G* pk = dK + hoff + (size_t)mykey * D + d0;
+                    G* pv = dV + hoff + (size_t)mykey * D + d0;
+                    if constexpr (sizeof(G) == 4) {
+                        f32x4 a, bb;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { a[e] = dkacc[dt][4 * g4 + e] * scale; bb[e] = dvacc[dt][4 * g4 + e]; }
+                        *reinterpret_cast<f32x4*>(pk) = a;
+                        *reinterpret_cast<f32x4*>(pv) = bb;
+                    } else {
+                        bf16x4 a, bb;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { a[e] = to_bf16(dkacc[dt][4 * g4 + e] * scale); bb[e] = to_bf16(dvacc[dt][4 * g4 + e]); }
+                        *reinterpret_cast<bf16x4*>(pk) = a;
+                        *reinterpret_cast<bf16x4*>(pv) = bb;
+                    }
+                }
+            }
+    }
+}
+
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, long n4)
 {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -474,11 +728,19 @@ static hipError_t main_t(const void* Q, const void* K, const void* V, const void
                          const float* Dd, int BH, int N, float scale, float* dQacc, void* dK, void* dV,
                          hipStream_t st)
 {
-    using C = BwdCfg<T, D>;
-    const int nkblk = (N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL, G>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, LSE, Dd, dQacc, (G*)dK,
-                       (G*)dV, N, nkblk, scale);
+    if constexpr (sizeof(T) == 2) {
+        using C = BwdBf16Cfg<D>;
+        const int nkblk = (N + C::BN - 1) / C::BN;
+        hipLaunchKernelGGL((bwd_kernel_bf16<D, CAUSAL, G>), dim3(nkblk * BH), dim3(256), 0, st,
+                           (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, dQacc,
+                           (G*)dK, (G*)dV, N, nkblk, scale);
+    } else {
+        using C = BwdCfg<T, D>;
+        const int nkblk = (N + C::BN - 1) / C::BN;
+        hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL, G>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, LSE, Dd, dQacc, (G*)dK,
+                           (G*)dV, N, nkblk, scale);
+    }
     return hipGetLastError();
 }
 

@@ -74,6 +74,138 @@ __device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
+// ---- LDS tiles written by direct-to-LDS loads (no padding possible) ----
+// Rows of RB = 256 bytes (16 slots of 16 B) or 128 bytes (8 slots).  Logical
+// 16-byte chunk c of row r lives in slot swz(r, c).  The XOR masks are chosen so
+// that (a) 16 lanes reading the same chunk of 16 consecutive rows and (b) the
+// transpose-read pattern (4 consecutive rows x 2 adjacent chunks per 16 lanes)
+// both hit distinct bank groups.
+template <int RB>
+__device__ __forceinline__ int swz(int r, int c)
+{
+    if constexpr (RB == 256) {
+        return c ^ (((r & 3) << 1) | ((r >> 2) & 1) | (r & 8));
+    } else {
+        const int x = (r >> 1) & 7;
+        return c ^ (((x & 1) << 1) | ((x >> 1) & 1) | (x & 4));
+    }
+}
+
+// Byte offset of bf16 element (r, col) inside an RB-row tile.
+template <int RB>
+__device__ __forceinline__ int tile_off(int r, int col)
+{
+    return r * RB + swz<RB>(r, col >> 3) * 16 + (col & 7) * 2;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// One ds_read_b64_tr_b16.  Within each group of 16 lanes, lane i receives
+// element (i % 4) of the 8-byte reads made by lanes 4k + i/4 of its group, k = 0..3
+// (layout measured on gfx950).
+__device__ __forceinline__ u32x2 lds_tr16(const char* p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand fragment (8 bf16) for a lane that needs X[k][m] with
+// m = m0 + lane % 32 and k = k0 + 8*(e/4) + 4*(lane/32) + e%4, e = 0..7, read
+// from a row-major (k rows, m columns) bf16 tile in LDS: two transpose reads.
+template <int RB>
+__device__ __forceinline__ bf16x8 ld_frag_tr(const char* tile, int k0, int m0, int lane)
+{
+    const int g = lane >> 4, j = lane & 15;
+    const int row = k0 + 4 * (g >> 1) + (j >> 2);
+    const int col = m0 + 16 * (g & 1) + 4 * (j & 3);
+    const u32x2 a = lds_tr16(tile + tile_off<RB>(row, col));
+    const u32x2 b = lds_tr16(tile + tile_off<RB>(row + 8, col));
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// MFMA operand fragment (8 bf16) for a lane that needs X[m][k] with
+// m = m0 + lane % 32 and k = k0 + 8*(lane/32) .. +7: one 16-byte row read.
+template <int RB>
+__device__ __forceinline__ bf16x8 ld_frag_row(const char* tile, int m0, int k0, int lane)
+{
+    const int row = m0 + (lane & 31);
+    const int c = (k0 >> 3) + (lane >> 5);
+    return __builtin_bit_cast(bf16x8, ld16(tile + row * RB + swz<RB>(row, c) * 16));
+}
+
+// Direct-to-LDS copy of `rows` rows of a bf16 [*, D] array into an RB-row tile
+// (swizzled), by one wave: each instruction moves 1 KB.  `r` covers the source
+// rows (rows past its end read as zeros); chunks past D are filled with zeros.
+template <int D, int RB>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, char* tile, int row0, int rows, int lane)
+{
+    constexpr int SLOTS = RB / 16, ROWS_PER = 1024 / RB, CPR = D / 8;
+    for (int base = row0; base < row0 + rows; base += ROWS_PER) {
+        const int row = base + lane / SLOTS;
+        const int c = swz<RB>(row, lane % SLOTS);             // swz is an involution in c
+        const uint32_t off = c < CPR ? (uint32_t)(row * D * 2 + c * 16) : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(tile + base * RB),
+                                                 16, off, 0, 0, 0);
+    }
+}
+
+// Per-lane byte offsets into RB-row swizzled tiles, computed once, so that every
+// fragment read in a loop is (lane offset) + (compile-time constant).
+//   row(m0, s): ld_frag_row(tile, m0, 16 s) for m0 a multiple of 16
+//   tr(k0, j):  ld_frag_tr(tile, k0, 32 j) for k0 a multiple of 16; the second of
+//               the two transpose reads sits at a constant distance from the first.
+template <int RB, int NKS>
+struct TileLane {
+    int ro[NKS];
+    int tr0, tr1;
+    __device__ __forceinline__ void init(int lane)
+    {
+        const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) ro[s] = l32 * RB + swz<RB>(l32, 2 * s + h) * 16;
+        const int g = lane >> 4, j = lane & 15;
+        const int rl = 4 * (g >> 1) + (j >> 2);            // row within the 8-row group
+        const int cl = 16 * (g & 1) + 4 * (j & 3);         // column within the 32-column tile
+        const int T = swz<RB>(rl, cl >> 3);                // slot for column tile 0
+        tr0 = rl * RB + T * 16 + ((cl >> 2) & 1) * 8;
+        if constexpr (RB == 256) tr1 = rl * RB + (T ^ 4) * 16 + ((cl >> 2) & 1) * 8;
+        else tr1 = tr0;
+    }
+    __device__ __forceinline__ bf16x8 row(const char* tile, int m0, int s) const
+    {
+        return __builtin_bit_cast(bf16x8, ld16(tile + m0 * RB + ro[s]));
+    }
+    __device__ __forceinline__ bf16x8 tr(const char* tile, int k0, int jt) const
+    {
+        int o, o2;
+        if constexpr (RB == 256) {
+            o = k0 * RB + ((jt & 2) ? 128 : 0) + ((jt & 1) ? tr1 : tr0);
+            o2 = o + 8 * RB + ((jt & 2) ? -128 : 128);
+        } else {
+            o = k0 * RB + (jt ? 64 : 0) + tr0;
+            o2 = o + 8 * RB + (jt ? -64 : 64);
+        }
+        const u32x2 a = lds_tr16(tile + o);
+        const u32x2 b = lds_tr16(tile + o2);
+        return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+    }
+};
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// s_waitcnt vmcnt(n) (other counters left unconstrained), n <= 63: waits until at
+// most n vector-memory instructions of this wave are outstanding.
+__device__ __forceinline__ void wait_vmem_leave(int n)
+{
+    switch (n) {   // the immediate must be a constant
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 16: __builtin_amdgcn_s_waitcnt(0x0F70 | (16 & 15) | ((16 >> 4) << 14)); break;
+        case 32: __builtin_amdgcn_s_waitcnt(0x0F70 | (32 & 15) | ((32 >> 4) << 14)); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
 // max(a, b, c) in one v_max3_f32.
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 

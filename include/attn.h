@@ -17,8 +17,8 @@
  * Conventions shared by every entry point
  *   - Q, K, V, O, dO, dQ, dK, dV are device pointers to contiguous row-major
  *     [B, H, N, d] arrays (d fastest).  LSE and D are device fp32 [B, H, N].
- *   - d must be 64, 80 or 128 (else ATTN_EUNSUPPORTED).  B, H, N >= 1 and
- *     B*H*N*d < 2^31 (else ATTN_EINVAL).  Q, K, V have the same N.
+ *   - d must be 64, 80 or 128 (else ATTN_EUNSUPPORTED).  B, H, N >= 1,
+ *     B*H*N*d < 2^31 and N*d < 2^29 (else ATTN_EINVAL).  Q, K, V have the same N.
  *   - scale must be finite (else ATTN_EINVAL); its sign is arbitrary.
  *   - Every pointer must be non-NULL and 16-byte aligned (else ATTN_EINVAL).
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).
