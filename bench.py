@@ -1,8 +1,8 @@
 """Benchmark of the attention hot path on one MI355X.
 
 One step = forward (attn_fwd) + backward preprocess (attn_bwd_preprocess) +
-backward main pass (attn_bwd_main) over one batch of resident synthetic
-inputs: the whole path, fwd and bwd.  Default workload: B=4, H=16, N=4096,
+key-side backward (attn_bwd_dkdv) + query-side backward (attn_bwd_dq) over one
+batch of resident synthetic inputs: the whole path, fwd and bwd.  Default workload: B=4, H=16, N=4096,
 d=128, causal, bf16 (the N = 4k case of the headline metric); the N = 16k case
 (B=1, H=16) is measured in the same run and reported under "secondary".
 
@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 
 import torch  # noqa: E402
 
-from exact_tiled_attention_12_amd import attn_bwd_main, attn_bwd_preprocess, attn_fwd  # noqa: E402
+from exact_tiled_attention_12_amd import attn_bwd_dkdv, attn_bwd_dq, attn_bwd_preprocess, attn_fwd  # noqa: E402
 from exact_tiled_attention_12_amd.configs import CONFIGS  # noqa: E402
 from exact_tiled_attention_12_amd.flops import attn_flops  # noqa: E402
 from exact_tiled_attention_12_amd.inputs import config_inputs  # noqa: E402
@@ -63,22 +63,25 @@ class Workload:
         self.fl_fwd = attn_flops(B, H, N, d, cfg.causal, "fwd")
         self.fl_bwd = attn_flops(B, H, N, d, cfg.causal, "bwd")
 
+    KERNELS = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
+
     def step(self, ev=None):
         c = self.cfg
-        if ev is not None:
-            ev[0].record()
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
         attn_fwd(self.q, self.k, self.v, causal=c.causal, out=self.o, lse=self.lse)
-        if ev is not None:
-            ev[1].record()
-        attn_bwd_preprocess(self.o, self.do, D=self.D, dq_acc=self.dq)
-        if ev is not None:
-            ev[2].record()
-        attn_bwd_main(self.q, self.k, self.v, self.do, self.lse, self.D, self.dq, causal=c.causal,
-                      dk=self.dk, dv=self.dv)
-        if ev is not None:
-            ev[3].record()
+        rec(1)
+        if not c.backward:
+            return
+        attn_bwd_preprocess(self.o, self.do, D=self.D)
+        rec(2)
+        attn_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.D, causal=c.causal, dk=self.dk, dv=self.dv)
+        rec(3)
+        attn_bwd_dq(self.q, self.k, self.v, self.do, self.lse, self.D, causal=c.causal, dq=self.dq)
+        rec(4)
 
     def measure(self, steps, warmup):
+        """Returns (wall seconds per step, {kernel: mean seconds per launch})."""
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -88,15 +91,14 @@ class Workload:
             self.step()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
-        # per-kernel durations from events on the kernels' stream
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        # per-kernel durations from events on the kernels' stream (a second pass)
+        nk = len(self.KERNELS) if self.cfg.backward else 1
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
         for e in evs:
             self.step(e)
         torch.cuda.synchronize()
-        fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e-3
-        pre = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e-3
-        main = sum(e[2].elapsed_time(e[3]) for e in evs) / steps * 1e-3
-        return wall, fwd, pre, main
+        per = {self.KERNELS[i]: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps * 1e-3 for i in range(nk)}
+        return wall, per
 
 
 def cpu_baseline(cfg, budget_s=12.0):
@@ -166,42 +168,47 @@ def main():
     cfg = CONFIGS[args.config]
     log(f"bench: workload {cfg.index} ({cfg.name}), warmup {args.warmup}, steps {args.steps}")
     w = Workload(cfg, dev)
-    wall, t_fwd, t_pre, t_main = w.measure(args.steps, args.warmup)
+    wall, per = w.measure(args.steps, args.warmup)
     flops = w.fl_fwd + (w.fl_bwd if cfg.backward else 0.0)
     value = flops / wall / 1e12
-    fwd_tf = w.fl_fwd / t_fwd / 1e12
-    bwd_tf = w.fl_bwd / (t_pre + t_main) / 1e12
-    main_tf = w.fl_bwd / t_main / 1e12
-    log(f"bench: step {wall * 1e3:.3f} ms; fwd {t_fwd * 1e6:.1f} us ({fwd_tf:.1f} TFLOP/s), "
-        f"bwd_pre {t_pre * 1e6:.1f} us, bwd_main {t_main * 1e6:.1f} us ({main_tf:.1f} TFLOP/s)")
     B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    # algorithmic FLOPs per launch: forward 4 N^2 d per head; the backward's 2.5x
+    # split as the key side's 4 products (2.0x) and the query side's 3 (1.5x)
+    # minus the recomputed S and dP both sides share (counted once, on the key side)
+    kflops = {"attn_fwd": w.fl_fwd, "attn_bwd_dkdv": 2.0 * w.fl_fwd, "attn_bwd_dq": 0.5 * w.fl_fwd}
+    kern = {}
+    for name, t in per.items():
+        ent = {"us": round(t * 1e6, 2)}
+        if name in kflops:
+            tf = kflops[name] / t / 1e12
+            ent.update(tflops=round(tf, 2), frac_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        kern[name] = ent
+    t_bwd = sum(t for n, t in per.items() if n != "attn_fwd")
+    if cfg.backward:
+        kern["bwd_total_tflops"] = round(w.fl_bwd / t_bwd / 1e12, 2)
+        kern["bwd_frac_peak"] = round(w.fl_bwd / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 4)
+    kern["fwd_frac_peak"] = round(w.fl_fwd / per["attn_fwd"] / 1e12 / PEAK_BF16_TFLOPS, 4)
+    log("bench: step %.3f ms; " % (wall * 1e3) + ", ".join(f"{n} {t * 1e6:.1f} us" for n, t in per.items()) +
+        f"; fwd {w.fl_fwd / per['attn_fwd'] / 1e12:.1f} TFLOP/s" +
+        (f", bwd {w.fl_bwd / t_bwd / 1e12:.1f} TFLOP/s" if cfg.backward else ""))
 
-    # dominant kernel = the one with the largest share of the step
-    kern = {"attn_bwd_main": (t_main, w.fl_bwd), "attn_fwd": (t_fwd, w.fl_fwd)}
-    dom = max(kern, key=lambda n: kern[n][0])
-    t_dom, fl_dom = kern[dom]
-    achieved = fl_dom / t_dom / 1e12
+    # dominant kernel = the largest share of the step
+    dom = max((n for n in per if n in kflops), key=lambda n: per[n])
+    achieved = kflops[dom] / per[dom] / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "algorithmic_flop_per_launch": fl_dom, "avg_launch_us": round(t_dom * 1e6, 2),
+                "algorithmic_flop_per_launch": kflops[dom], "avg_launch_us": round(per[dom] * 1e6, 2),
                 "traffic": load_traffic(dom)}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"attention fwd+bwd, B={B} H={H} N={N} d={d} causal={cfg.causal} bf16 "
-                               f"(Q,K,V,dO ~ N(0,1), seed {cfg.seed})",
+        "config": {"workload": f"attention {'fwd+bwd' if cfg.backward else 'fwd'}, B={B} H={H} N={N} d={d} "
+                               f"causal={cfg.causal} bf16 (Q,K,V,dO ~ N(0,1), seed {cfg.seed})",
                    "global_batch": B, "seq_len": N, "heads": H, "head_dim": d, "causal": cfg.causal,
                    "parallelism": "single GPU"},
-        "kernels": {
-            "attn_fwd": {"us": round(t_fwd * 1e6, 2), "tflops": round(fwd_tf, 2),
-                         "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
-            "attn_bwd_preprocess": {"us": round(t_pre * 1e6, 2)},
-            "attn_bwd_main": {"us": round(t_main * 1e6, 2), "tflops": round(main_tf, 2),
-                              "frac_peak": round(main_tf / PEAK_BF16_TFLOPS, 4)},
-            "bwd_total_tflops": round(bwd_tf, 2), "bwd_frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-        },
+        "kernels": kern,
         "roofline": roofline,
         "source_hash": source_hash(),
     }
@@ -213,17 +220,19 @@ def main():
         log("bench: secondary workload 4 (N=16384)")
         w4 = Workload(cfg4, dev)
         steps4 = max(3, args.steps // 2)
-        wall4, f4, p4, m4 = w4.measure(steps4, max(2, args.warmup // 2))
+        wall4, per4 = w4.measure(steps4, max(2, args.warmup // 2))
+        tb4 = sum(t for n, t in per4.items() if n != "attn_fwd")
         out["secondary"] = {
-            "workload": f"B=1 H=16 N=16384 d=128 causal bf16 (Q,K x0.5)", "steps": steps4,
+            "workload": "B=1 H=16 N=16384 d=128 causal bf16 (Q,K x0.5)", "steps": steps4,
             "ms_per_step": round(wall4 * 1e3, 4),
             "value": round((w4.fl_fwd + w4.fl_bwd) / wall4 / 1e12, 2),
-            "fwd_tflops": round(w4.fl_fwd / f4 / 1e12, 2),
-            "fwd_frac_peak": round(w4.fl_fwd / f4 / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "bwd_tflops": round(w4.fl_bwd / (p4 + m4) / 1e12, 2),
-            "bwd_frac_peak": round(w4.fl_bwd / (p4 + m4) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fwd_tflops": round(w4.fl_fwd / per4["attn_fwd"] / 1e12, 2),
+            "fwd_frac_peak": round(w4.fl_fwd / per4["attn_fwd"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_tflops": round(w4.fl_bwd / tb4 / 1e12, 2),
+            "bwd_frac_peak": round(w4.fl_bwd / tb4 / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels_us": {n: round(t * 1e6, 2) for n, t in per4.items()},
         }
-        log(f"bench: N=16384 step {wall4 * 1e3:.3f} ms")
+        log(f"bench: N=16384 step {wall4 * 1e3:.3f} ms; " + ", ".join(f"{n} {t * 1e6:.1f} us" for n, t in per4.items()))
 
     if not args.no_cpu:
         log("bench: CPU oracle baseline")

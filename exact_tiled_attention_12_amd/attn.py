@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_workspace_bytes",
-            "attn_bwd", "attn_status_str", "attn_last_hip_error")
+EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
+            "attn_bwd_workspace_bytes", "attn_bwd", "attn_status_str", "attn_last_hip_error")
 
 _lib = None
 
@@ -42,12 +42,15 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.attn_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
-        L.attn_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, vp, vp]
+        L.attn_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
+        L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
+        L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
         L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp]
-        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = sz
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, i, vp, sz, vp]
-        for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_main", "attn_bwd"):
+        for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
+                     "attn_bwd"):
             getattr(L, name).restype = i
         L.attn_status_str.argtypes = [i]
         L.attn_status_str.restype = ctypes.c_char_p
@@ -114,32 +117,55 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None)
     return o, l
 
 
-def attn_bwd_workspace_bytes(B, H, N, d, grad_dtype=torch.float32):
-    return int(lib().attn_bwd_workspace_bytes(B, H, N, d, ATTN_BF16 if grad_dtype == torch.bfloat16 else ATTN_F32))
+def attn_bwd_workspace_bytes(B, H, N, d):
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d))
 
 
-def attn_bwd_preprocess(o, do, D=None, dq_acc=None, stream=None):
-    """D = rowsum(dO o O) (fp32 [B,H,N]) and dq_acc = 0 (fp32 [B,H,N,d])."""
+def attn_bwd_preprocess(o, do, D=None, stream=None):
+    """D = rowsum(dO o O), fp32 [B, H, N]."""
     B, H, N, d = _shape(o)
     _check_inputs(o, do)
     D = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if D is None else D
-    dq_acc = torch.empty((B, H, N, d), dtype=torch.float32, device=o.device) if dq_acc is None else dq_acc
-    _call("attn_bwd_preprocess", _ptr(o), _ptr(do), _dt(o), B, H, N, d, _ptr(D), _ptr(dq_acc),
-          _stream(o, stream))
-    return D, dq_acc
+    _call("attn_bwd_preprocess", _ptr(o), _ptr(do), _dt(o), B, H, N, d, _ptr(D), _stream(o, stream))
+    return D
 
 
-def attn_bwd_main(q, k, v, do, lse, D, dq_acc, scale=None, causal=False, dk=None, dv=None, stream=None):
-    """dK, dV (fp32, written) and dQ added into dq_acc.  Returns (dq_acc, dK, dV)."""
+def _grad(t, q):
     B, H, N, d = _shape(q)
-    _check_inputs(q, k, v, do, lse, D, dq_acc)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    dk = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dk is None else dk
-    dv = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if dv is None else dv
+    return torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if t is None else t
+
+
+def attn_bwd_dkdv(q, k, v, do, lse, D, scale=None, causal=False, dk=None, dv=None, stream=None):
+    """dK, dV (fp32, written once).  bf16 inputs only."""
+    B, H, N, d = _shape(q)
+    _check_inputs(q, k, v, do, lse, D)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dk, dv = _grad(dk, q), _grad(dv, q)
+    _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
+          float(scale), int(bool(causal)), _ptr(dk), _ptr(dv), _stream(q, stream))
+    return dk, dv
+
+
+def attn_bwd_dq(q, k, v, do, lse, D, scale=None, causal=False, dq=None, stream=None):
+    """dQ (fp32, written once).  bf16 inputs only."""
+    B, H, N, d = _shape(q)
+    _check_inputs(q, k, v, do, lse, D)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = _grad(dq, q)
+    _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
+          float(scale), int(bool(causal)), _ptr(dq), _stream(q, stream))
+    return dq
+
+
+def attn_bwd_main(q, k, v, do, lse, D, scale=None, causal=False, dq=None, dk=None, dv=None, stream=None):
+    """dQ, dK, dV (fp32, written once) given D from attn_bwd_preprocess."""
+    B, H, N, d = _shape(q)
+    _check_inputs(q, k, v, do, lse, D)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq, dk, dv = _grad(dq, q), _grad(dk, q), _grad(dv, q)
     _call("attn_bwd_main", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
-          float(scale), int(bool(causal)), _ptr(dq_acc), _ptr(dk), _ptr(dv), _stream(q, stream))
-    return dq_acc, dk, dv
+          float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _stream(q, stream))
+    return dq, dk, dv
 
 
 def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, grad_dtype=torch.float32, workspace=None,
@@ -150,7 +176,7 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, grad_dtype=torch.flo
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     gdt = ATTN_BF16 if grad_dtype == torch.bfloat16 else ATTN_F32
-    need = attn_bwd_workspace_bytes(B, H, N, d, grad_dtype)
+    need = attn_bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     mk = lambda t: torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) if t is None else t

@@ -65,36 +65,69 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, attn_dtype dt,
 }
 
 attn_status attn_bwd_preprocess(const void* O, const void* dO, attn_dtype dt, int B, int H, int N, int d,
-                                float* D, float* dQacc, void* stream)
+                                float* D, void* stream)
 {
     attn_status s = check_shape(B, H, N, d);
     if (s != ATTN_OK) return s;
     if (!dtype_ok(dt)) return ATTN_EINVAL;
-    if (!aligned16(O) || !aligned16(dO) || !aligned16(D) || !aligned16(dQacc)) return ATTN_EINVAL;
-    return from_hip(attn::launch_bwd_pre(O, dO, dt == ATTN_BF16, B * H, N, d, D, dQacc, (hipStream_t)stream));
+    if (!aligned16(O) || !aligned16(dO) || !aligned16(D)) return ATTN_EINVAL;
+    return from_hip(attn::launch_bwd_pre(O, dO, dt == ATTN_BF16, B * H, N, d, D, (hipStream_t)stream));
 }
 
-attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                          const float* D, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
-                          float* dQacc, float* dK, float* dV, void* stream)
+static attn_status check_bwd_args(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                                  const float* D, attn_dtype dt, int B, int H, int N, int d, float scale, int causal)
 {
     attn_status s = check_shape(B, H, N, d);
     if (s != ATTN_OK) return s;
     if (!dtype_ok(dt) || !isfinite(scale) || (causal != 0 && causal != 1)) return ATTN_EINVAL;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) ||
-        !aligned16(D) || !aligned16(dQacc) || !aligned16(dK) || !aligned16(dV))
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) || !aligned16(D))
         return ATTN_EINVAL;
-    return from_hip(attn::launch_bwd_main(Q, K, V, dO, LSE, D, dt == ATTN_BF16, B * H, N, d, scale, causal,
-                                          dQacc, dK, dV, false, (hipStream_t)stream));
+    return ATTN_OK;
 }
 
-size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype grad_dt)
+attn_status attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                          const float* D, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                          float* dK, float* dV, void* stream)
 {
-    if (check_shape(B, H, N, d) == ATTN_EINVAL || !dtype_ok(grad_dt)) return 0;
-    const size_t rows = (size_t)B * H * N;
-    size_t bytes = round256(rows * sizeof(float));
-    if (grad_dt == ATTN_BF16) bytes += round256(rows * (size_t)d * sizeof(float));
-    return bytes;
+    attn_status s = check_bwd_args(Q, K, V, dO, LSE, D, dt, B, H, N, d, scale, causal);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(dK) || !aligned16(dV)) return ATTN_EINVAL;
+    if (dt != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    return from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dK, dV, false,
+                                          (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                        const float* D, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                        float* dQ, void* stream)
+{
+    attn_status s = check_bwd_args(Q, K, V, dO, LSE, D, dt, B, H, N, d, scale, causal);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(dQ)) return ATTN_EINVAL;
+    if (dt != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false,
+                                        (hipStream_t)stream));
+}
+
+attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                          const float* D, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                          float* dQ, float* dK, float* dV, void* stream)
+{
+    attn_status s = check_bwd_args(Q, K, V, dO, LSE, D, dt, B, H, N, d, scale, causal);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(dQ) || !aligned16(dK) || !aligned16(dV)) return ATTN_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    if (dt == ATTN_F32)
+        return from_hip(attn::launch_bwd_f32(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, dK, dV, st));
+    attn_status r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dK, dV, false, st));
+    if (r != ATTN_OK) return r;
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false, st));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d)
+{
+    if (check_shape(B, H, N, d) == ATTN_EINVAL) return 0;
+    return round256((size_t)B * H * N * sizeof(float));
 }
 
 attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -102,29 +135,25 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                      void* dQ, void* dK, void* dV, attn_dtype grad_dt, void* workspace,
                      size_t workspace_bytes, void* stream)
 {
-    attn_status s = check_shape(B, H, N, d);
+    attn_status s = check_bwd_args(Q, K, V, dO, LSE, (const float*)workspace, dt, B, H, N, d, scale, causal);
     if (s != ATTN_OK) return s;
-    if (!dtype_ok(dt) || !dtype_ok(grad_dt) || !isfinite(scale) || (causal != 0 && causal != 1))
-        return ATTN_EINVAL;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
-        !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(workspace))
-        return ATTN_EINVAL;
-    if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, grad_dt)) return ATTN_EINVAL;
+    if (!dtype_ok(grad_dt)) return ATTN_EINVAL;
+    if (!aligned16(O) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV)) return ATTN_EINVAL;
+    if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_EINVAL;
+    if (dt == ATTN_F32 && grad_dt == ATTN_BF16) return ATTN_EUNSUPPORTED;
 
     hipStream_t st = (hipStream_t)stream;
     const bool bf_in = dt == ATTN_BF16, bf_grad = grad_dt == ATTN_BF16;
     const int BH = B * H;
-    const size_t rows = (size_t)BH * N;
     float* Dd = static_cast<float*>(workspace);
-    float* dQacc = bf_grad ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * sizeof(float)))
-                           : static_cast<float*>(dQ);
-    attn_status r = from_hip(attn::launch_bwd_pre(O, dO, bf_in, BH, N, d, Dd, dQacc, st));
+    attn_status r = from_hip(attn::launch_bwd_pre(O, dO, bf_in, BH, N, d, Dd, st));
     if (r != ATTN_OK) return r;
-    r = from_hip(attn::launch_bwd_main(Q, K, V, dO, LSE, Dd, bf_in, BH, N, d, scale, causal, dQacc, dK, dV,
-                                       bf_grad, st));
+    if (!bf_in)
+        return from_hip(attn::launch_bwd_f32(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, (float*)dQ, (float*)dK,
+                                             (float*)dV, st));
+    r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dK, dV, bf_grad, st));
     if (r != ATTN_OK) return r;
-    if (bf_grad) r = from_hip(attn::launch_f32_to_bf16(dQacc, dQ, (long)(rows * d), st));
-    return r;
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dQ, bf_grad, st));
 }
 
 }  // extern "C"

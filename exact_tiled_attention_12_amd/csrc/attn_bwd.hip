@@ -33,13 +33,12 @@
 namespace attn {
 
 // ----------------------------------------------------------------------------
-// Preprocess: D_i = sum_k dO_ik O_ik (fp32) and dQacc = 0.  Memory bound.
-// 8 lanes per row, 32 rows per 256-thread block.
+// Preprocess: D_i = sum_k dO_ik O_ik (fp32).  Memory bound: 8 lanes per row,
+// 32 rows per 256-thread block, 16-byte loads.
 // ----------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                      float* __restrict__ Dout,
-                                                      float* __restrict__ dQacc, long rows)
+                                                      float* __restrict__ Dout, long rows)
 {
     constexpr int CH = Mma<T>::CH, CPR = D / CH, LPR = 8;
     const long row = (long)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
@@ -60,16 +59,23 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
                 for (int e = 0; e < 4; ++e) acc = fmaf(av[e], bv[e], acc);
             }
         }
-        float* z = dQacc + row * D;
-        for (int x = u; x < D / 4; x += LPR) st16(z + 4 * x, zero4());
     }
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (row < rows && u == 0) Dout[row] = acc;
 }
 
+// Zero fill (a kernel rather than a memset, so callers may capture it in a graph).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, long n4)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) st16(p + 4 * i, zero4());
+}
+
 // ----------------------------------------------------------------------------
-// Main backward kernel.
+// fp32 backward (all three gradients in one kernel, dQ by fp32 atomics into a
+// zero-filled accumulator).  Used for fp32 inputs, where rows are twice as wide
+// and the bf16 tile layouts below do not apply.
 // ----------------------------------------------------------------------------
 template <typename T, int D>
 struct BwdCfg {
@@ -426,52 +432,44 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
 }
 
 // ----------------------------------------------------------------------------
-// Main backward kernel, bf16 inputs (the hot path).
-//
-// LDS, every tile in swizzled rows and written by direct-to-LDS loads except dS^T:
-//   sQ0/sQ1, sG0/sG1 : Q and dO rows of the current / next query block (row reads
-//                      for S = Q K^T and dP = dO V^T, transpose reads for Q^T, dO^T)
-//   sK               : the workgroup's BN key rows (row reads: B operand of S;
-//                      transpose reads: B operand of dQ = dS K)
-//   sS0/sS1          : dS^T [key][query] of the current / previous block
-//   sL*, sD*         : -LSE*log2 e and D of the block's rows
-// Each buffer is its own __shared__ object and the loop is unrolled by two, so
-// the compiler can tell the in-flight direct-to-LDS loads (next block) from the
-// LDS reads of the current block and does not wait for them.  One barrier per
-// query block: the dQ product of block i-1 runs after the barrier of block i.
+// bf16 backward, part 1: dK and dV.  One workgroup per BN = 128 keys (32 per
+// wave), iterating over query blocks of BM = 64 rows:
+//   S = Q K^T, dP = dO V^T       (accumulator lane = one key, rows = queries)
+//   P = exp2(S c2 - LSE log2 e), dS = P o (dP - D)
+//   dV^T += dO^T P,  dK^T += Q^T dS   (contraction over queries; dO^T and Q^T
+//                                      come from transpose reads of row tiles)
+// LDS: sQ*/sG* hold the Q and dO rows of the current and next block (direct-to-LDS
+// loads into swizzled rows), sK the workgroup's K rows (row reads give the B
+// operand of S).  Separate __shared__ objects and a loop unrolled by two let the
+// compiler see that the in-flight loads never alias the tiles being read.
 // ----------------------------------------------------------------------------
 template <int D>
-struct BwdBf16Cfg {
+struct BwdKVCfg {
     static constexpr int BN = 128, BM = 64, NQT = BM / 32;
-    static constexpr int RB = D == 64 ? 128 : 256;        // LDS bytes per Q/dO/K row
+    static constexpr int RB = D == 64 ? 128 : 256;        // LDS bytes per row
     static constexpr int DP = (D + 31) / 32 * 32, NDT = DP / 32;
     static constexpr int NKS = D / 16;
-    static constexpr int SRB = BM * 2;                    // bytes per dS^T row (128)
-    static constexpr int Q_BYTES = BM * RB, K_BYTES = BN * RB, S_BYTES = BN * SRB;
-    static constexpr int DQ_PER_WAVE = (NDT + 1) / 2;     // dQ head-dim tiles per wave
-    static constexpr int BYTES = 4 * Q_BYTES + K_BYTES + 2 * S_BYTES + 4 * BM * 4;
-    static_assert(BYTES <= 160 * 1024, "LDS budget");
-    static_assert(SRB == 128, "dS^T rows use the 128-byte swizzle");
+    static constexpr int Q_BYTES = BM * RB, K_BYTES = BN * RB;
+    static_assert(4 * Q_BYTES + K_BYTES + 4 * BM * 4 <= 160 * 1024, "LDS budget");
 };
 
 template <int D, bool CAUSAL, typename G>
-__global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                                                       const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                                                       const float* __restrict__ LSE, const float* __restrict__ Dg,
-                                                       float* __restrict__ dQacc, G* __restrict__ dK,
-                                                       G* __restrict__ dV, int N, int nkblk, float scale)
+__global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                     const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                                                     const float* __restrict__ LSE, const float* __restrict__ Dg,
+                                                     G* __restrict__ dK, G* __restrict__ dV, int N, int nkblk,
+                                                     float scale)
 {
-    using C = BwdBf16Cfg<D>;
+    using C = BwdKVCfg<D>;
     constexpr int RB = C::RB;
     constexpr uint32_t ROWB = D * 2;                    // global bytes per row
     __shared__ __attribute__((aligned(1024))) char sQ0[C::Q_BYTES], sQ1[C::Q_BYTES];
     __shared__ __attribute__((aligned(1024))) char sG0[C::Q_BYTES], sG1[C::Q_BYTES];
     __shared__ __attribute__((aligned(1024))) char sK[C::K_BYTES];
-    __shared__ __attribute__((aligned(1024))) char sS0[C::S_BYTES], sS1[C::S_BYTES];
     __shared__ __attribute__((aligned(16))) float sL0[C::BM], sL1[C::BM], sD0[C::BM], sD1[C::BM];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform (scalar branches)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
 
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -483,22 +481,18 @@ __global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ 
     const size_t hoff = (size_t)head * (size_t)N * D;
     const bf16* __restrict__ Qh = Q + hoff;
     const bf16* __restrict__ dOh = dO + hoff;
-    const uint32_t head_bytes = (uint32_t)N * ROWB;
     const float c2 = scale * kLog2e;
-    TileLane<RB, C::NKS> tl;            // Q, dO, K tiles
-    TileLane<128, 1> ts;                // dS^T tiles
+    TileLane<RB, C::NKS> tl;
     tl.init(lane);
-    ts.init(lane);
 
-    // ---- resident V fragments (B operand of dP = dO V^T) ----
+    // resident V fragments (B operand of dP = dO V^T); K rows to LDS (B operand of S)
     bf16x8 vf[C::NKS];
     {
-        const auto rv = make_rsrc(V + hoff, head_bytes);
+        const auto rv = make_rsrc(V + hoff, (uint32_t)N * ROWB);
         const uint32_t ro = (uint32_t)mykey * ROWB + 16 * h;
 #pragma unroll
         for (int s = 0; s < C::NKS; ++s) vf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rv, ro + 32 * s));
     }
-    // ---- the workgroup's K rows in LDS ----
     dma_rows<D, RB>(make_rsrc(K + hoff + (size_t)k0 * D, (uint32_t)(N - k0) * ROWB), sK, wave * (C::BN / 4),
                     C::BN / 4, lane);
 
@@ -510,16 +504,11 @@ __global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ 
 
     const int nq = (N + C::BM - 1) / C::BM;
     const int i0 = CAUSAL ? (k0 / C::BM) : 0;
-    const auto rdq = make_rsrc(dQacc + hoff, (uint32_t)N * D * 4);
-    // vector-memory instructions one dq phase issues on this wave (all atomics)
-    constexpr int dq_vm = 16 * C::DQ_PER_WAVE;
 
-    // Loads of query block i: Q and dO rows by DMA (16 rows per wave each);
-    // -LSE*log2e (wave 0) and D (wave 1) into a register, parked in LDS later.
     float lreg = 0.f;
     auto issue_block = [&](int i, char* sQ, char* sG) {
         const int q0 = i * C::BM;
-        const uint32_t bytes = (uint32_t)(N - q0) * ROWB;
+        const uint32_t bytes = (uint32_t)(N - q0) * ROWB;         // rows past N read as zeros
         dma_rows<D, RB>(make_rsrc(Qh + (size_t)q0 * D, bytes), sQ, wave * (C::BM / 4), C::BM / 4, lane);
         dma_rows<D, RB>(make_rsrc(dOh + (size_t)q0 * D, bytes), sG, wave * (C::BM / 4), C::BM / 4, lane);
         if (wave == 0)
@@ -527,38 +516,7 @@ __global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ 
         if (wave == 1) lreg = buf_ld4f(make_rsrc(Dg + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
     };
 
-    // dQ[q][d] += scale * sum_key dS[q][key] K[key][d] for query block i from dS^T.
-    // Wave w: query tile w % 2, head-dim tiles w / 2 and w / 2 + 2.
-    auto dq_phase = [&](int i, const char* sS) {
-        const int qt = wave & 1;
-        f32x16 acc[C::DQ_PER_WAVE];
-#pragma unroll
-        for (int x = 0; x < C::DQ_PER_WAVE; ++x)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[x][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < C::BN / 16; ++s) {
-            const bf16x8 af = ts.tr(sS, 16 * s, qt);
-#pragma unroll
-            for (int x = 0; x < C::DQ_PER_WAVE; ++x)      // for d = 80, tile 3 reads zero columns
-                acc[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, tl.tr(sK, 16 * s, (wave >> 1) + 2 * x), acc[x], 0, 0, 0);
-        }
-#pragma unroll
-        for (int x = 0; x < C::DQ_PER_WAVE; ++x) {
-            const int dt = (wave >> 1) + 2 * x;
-            const int dcol = 32 * dt + l32;
-            if (dcol < D) {
-                const uint32_t base = (uint32_t)(i * C::BM + 32 * qt + 4 * h) * (D * 4) + dcol * 4;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[x][r] * scale, rdq,
-                                                                    (int)(base + (8 * (r >> 2) + (r & 3)) * (D * 4)), 0, 0);
-            }
-        }
-    };
-
-    // One query block: S, dP, P, dS, dS^T -> LDS, dV += dO^T P, dK += Q^T dS.
-    auto block_body = [&](int i, const char* sQ, const char* sG, char* sS, const float* sL, const float* sD) {
+    auto block_body = [&](int i, const char* sQ, const char* sG, const float* sL, const float* sD) {
         const int q0 = i * C::BM;
         f32x16 sacc[C::NQT], pacc[C::NQT];
 #pragma unroll
@@ -574,7 +532,6 @@ __global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ 
                 pacc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sG, 32 * qt, s), vf[s], pacc[qt], 0, 0, 0);
             }
         }
-        // P = exp2(S c2 - LSE log2 e);  dS = P o (dP - D);  both to bf16
         // (a wave whose keys all follow the block's queries gets P = 0 from the mask;
         // skipping it instead would split the accumulators' live ranges)
         const bool need_mask = CAUSAL && (q0 < k0w + 31);
@@ -589,32 +546,18 @@ __global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ 
                 float p[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(sacc[qt][4 * g4 + e], c2, l4[e]));
-                if (need_mask) {              // diagonal blocks only: key > query -> 0
+                if (need_mask) {              // key > query -> 0
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (mykey > q0 + qo + e) p[e] = 0.f;
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float ds = p[e] * (pacc[qt][4 * g4 + e] - d4[e]);
                     pb[qt][g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e]);
-                    sb[qt][g4 >> 1][4 * (g4 & 1) + e] = to_bf16(ds);
+                    sb[qt][g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e] * (pacc[qt][4 * g4 + e] - d4[e]));
                 }
             }
         }
-        // dS^T -> LDS (rows = keys, 4 consecutive queries per 8-byte write)
-        {
-            const int row = 32 * wave + l32;
-#pragma unroll
-            for (int qt = 0; qt < C::NQT; ++qt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const u32x4 w = __builtin_bit_cast(u32x4, sb[qt][g4 >> 1]);
-                    const u32x2 v2 = (g4 & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-                    *reinterpret_cast<u32x2*>(sS + row * C::SRB + swz<128>(row, 4 * qt + g4) * 16 + 8 * h) = v2;
-                }
-        }
-        // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over the block's queries)
 #pragma unroll
         for (int qt = 0; qt < C::NQT; ++qt)
 #pragma unroll
@@ -627,31 +570,24 @@ __global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ 
                 }
     };
 
-    // One step of the pipeline for block i with static buffers (cur = block i, nxt = block i+1).
-    auto step = [&](int i, char* qc, char* gc, char* sc, float* lc, float* dc, char* qn, char* gn, char* sn) {
-        // block i's Q/dO/stat loads are in flight since the previous step; the dQ atomics
-        // issued after them may stay in flight (vector memory completes in issue order)
-        if (i > i0 + 1) wait_vmem_leave(dq_vm);
-        else wait_vmem_all();
+    auto step = [&](int i, char* qc, char* gc, float* lc, float* dc, char* qn, char* gn) {
+        wait_vmem_all();                                // this wave's loads of block i landed
         if (wave == 0) lc[lane] = lreg;
         if (wave == 1) dc[lane] = lreg;
-        __syncthreads();
+        __syncthreads();                                // everyone's loads landed; block i-1 fully read
         if (i + 1 < nq) issue_block(i + 1, qn, gn);
-        if (i > i0) dq_phase(i - 1, sn);                // dS^T of block i-1 lives in the other buffer
-        block_body(i, qc, gc, sc, lc, dc);
+        block_body(i, qc, gc, lc, dc);
     };
 
     issue_block(i0, sQ0, sG0);
     int i = i0;
     for (; i + 1 < nq; i += 2) {
-        step(i, sQ0, sG0, sS0, sL0, sD0, sQ1, sG1, sS1);
-        step(i + 1, sQ1, sG1, sS1, sL1, sD1, sQ0, sG0, sS0);
+        step(i, sQ0, sG0, sL0, sD0, sQ1, sG1);
+        step(i + 1, sQ1, sG1, sL1, sD1, sQ0, sG0);
     }
-    if (i < nq) step(i, sQ0, sG0, sS0, sL0, sD0, sQ1, sG1, sS1);
-    __syncthreads();
-    dq_phase(nq - 1, ((nq - 1 - i0) & 1) ? sS1 : sS0);
+    if (i < nq) step(i, sQ0, sG0, sL0, sD0, sQ1, sG1);
 
-    // ---- dK = scale * dK^T acc, dV = dV^T acc, written once ----
+    // dK = scale * dK^T acc, dV = dV^T acc, written once
     if (mykey < N) {
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
@@ -679,6 +615,165 @@ __global__ __launch_bounds__(256) void bwd_kernel_bf16(const bf16* __restrict__ 
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 backward, part 2: dQ.  One workgroup per BM = 128 query rows (32 per
+// wave, two workgroups per CU), iterating over key tiles of BN = 64 -- the same
+// shape as the forward, and the same trick: work on transposes so that every
+// accumulator lane holds ONE query.
+//   S^T = K Q^T, dP^T = V dO^T        (A = K, V row reads; B = Q, dO registers)
+//   P^T = exp2(S^T c2 - LSE log2 e), dS^T = P^T o (dP^T - D)   (per-lane LSE, D)
+//   dQ^T += K^T dS^T                   (A = K^T by transpose reads; B = dS^T from
+//                                       the accumulator registers, bf16)
+// dQ is written once (no atomics, deterministic).
+// ----------------------------------------------------------------------------
+template <int D>
+struct BwdQCfg {
+    static constexpr int BM = 128, BN = 64, NKT = BN / 32;
+    static constexpr int RB = D == 64 ? 128 : 256;
+    static constexpr int DP = (D + 31) / 32 * 32, NDT = DP / 32;
+    static constexpr int NKS = D / 16;
+    static constexpr int T_BYTES = BN * RB;
+    static_assert(4 * T_BYTES <= 80 * 1024, "two workgroups per CU");
+};
+
+template <int D, bool CAUSAL, typename G>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                                                      const float* __restrict__ LSE, const float* __restrict__ Dg,
+                                                      G* __restrict__ dQ, int N, int nqblk, float scale)
+{
+    using C = BwdQCfg<D>;
+    constexpr int RB = C::RB;
+    constexpr uint32_t ROWB = D * 2;
+    __shared__ __attribute__((aligned(1024))) char sK0[C::T_BYTES], sK1[C::T_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sV0[C::T_BYTES], sV1[C::T_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = bid / nqblk;
+    int qb = bid - head * nqblk;
+    if (CAUSAL) qb = nqblk - 1 - qb;                 // heavy row blocks first
+    const int q0 = qb * C::BM;
+    const int q0w = q0 + 32 * wave;
+    const int myq = q0w + l32;
+    const size_t hoff = (size_t)head * (size_t)N * D;
+    const bf16* __restrict__ Kh = K + hoff;
+    const bf16* __restrict__ Vh = V + hoff;
+    const float c2 = scale * kLog2e;
+    TileLane<RB, C::NKS> tl;
+    tl.init(lane);
+
+    // Q and dO fragments (B operands), this lane's -LSE*log2e and D
+    bf16x8 qf[C::NKS], gf[C::NKS];
+    float nlse, dq_d;
+    {
+        const uint32_t hb = (uint32_t)N * ROWB;
+        const auto rq = make_rsrc(Q + hoff, hb), rg = make_rsrc(dO + hoff, hb);
+        const uint32_t ro = (uint32_t)myq * ROWB + 16 * h;
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+            qf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rq, ro + 32 * s));
+            gf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rg, ro + 32 * s));
+        }
+        nlse = -kLog2e * buf_ld4f(make_rsrc(LSE + (size_t)head * N, (uint32_t)N * 4), myq * 4);
+        dq_d = buf_ld4f(make_rsrc(Dg + (size_t)head * N, (uint32_t)N * 4), myq * 4);
+    }
+
+    f32x16 dqacc[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.f;
+
+    const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+    const int ntiles = (kv_end + C::BN - 1) / C::BN;
+
+    auto issue_tile = [&](int j, char* sK, char* sV) {
+        const int kv0 = j * C::BN;
+        const uint32_t bytes = (uint32_t)(N - kv0) * ROWB;        // rows past N read as zeros
+        dma_rows<D, RB>(make_rsrc(Kh + (size_t)kv0 * D, bytes), sK, wave * (C::BN / 4), C::BN / 4, lane);
+        dma_rows<D, RB>(make_rsrc(Vh + (size_t)kv0 * D, bytes), sV, wave * (C::BN / 4), C::BN / 4, lane);
+    };
+
+    auto tile_body = [&](int j, const char* sK, const char* sV) {
+        const int kv0 = j * C::BN;
+        f32x16 sacc[C::NKT], pacc[C::NKT];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { sacc[kt][r] = 0.f; pacc[kt][r] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt) {
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sK, 32 * kt, s), qf[s], sacc[kt], 0, 0, 0);
+                pacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sV, 32 * kt, s), gf[s], pacc[kt], 0, 0, 0);
+            }
+        // key kv0 + 32 kt + 8 (r/4) + 4 h + r%4 of this lane's query
+        const bool need_mask = CAUSAL && (kv0 + C::BN - 1 > q0w);
+        bf16x8 sb[C::NKT][2];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(sacc[kt][r], c2, nlse));
+                if (need_mask && kv0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3) > myq) p = 0.f;
+                sb[kt][r >> 3][r & 7] = to_bf16(p * (pacc[kt][r] - dq_d));
+            }
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt)
+                    dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sK, 32 * kt + 16 * s2, dt), sb[kt][s2],
+                                                                        dqacc[dt], 0, 0, 0);
+    };
+
+    auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
+        wait_vmem_all();
+        __syncthreads();
+        if (j + 1 < ntiles) issue_tile(j + 1, kn, vn);
+        if (!(CAUSAL && j * C::BN > q0w + 31))          // else every key of the tile follows this wave's rows
+            tile_body(j, kc, vc);
+    };
+
+    issue_tile(0, sK0, sV0);
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+        step(j, sK0, sV0, sK1, sV1);
+        step(j + 1, sK1, sV1, sK0, sV0);
+    }
+    if (j < ntiles) step(j, sK0, sV0, sK1, sV1);
+
+    // dQ = scale * dQ^T acc (lane = query; 4 consecutive head-dim values per store)
+    if (myq < N) {
+        G* dst = dQ + hoff + (size_t)myq * D;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * dt + 8 * g4 + 4 * h;
+                if (d0 < D) {
+                    if constexpr (sizeof(G) == 4) {
+                        f32x4 a;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) a[e] = dqacc[dt][4 * g4 + e] * scale;
+                        *reinterpret_cast<f32x4*>(dst + d0) = a;
+                    } else {
+                        bf16x4 a;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) a[e] = to_bf16(dqacc[dt][4 * g4 + e] * scale);
+                        *reinterpret_cast<bf16x4*>(dst + d0) = a;
+                    }
+                }
+            }
+    }
+}
+
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, long n4)
 {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -695,84 +790,107 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
 // launchers
 // ----------------------------------------------------------------------------
 template <typename T, int D>
-static hipError_t pre_t(const void* O, const void* dO, int BH, int N, float* Dd, float* dQacc, hipStream_t st)
+static hipError_t pre_t(const void* O, const void* dO, int BH, int N, float* Dd, hipStream_t st)
 {
     const long rows = (long)BH * N;
-    const long blocks = (rows + 31) / 32;
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st, (const T*)O,
-                       (const T*)dO, Dd, dQacc, rows);
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, (const T*)O,
+                       (const T*)dO, Dd, rows);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_pre(const void* O, const void* dO, bool bf16_in, int BH, int N, int d, float* Dd,
-                          float* dQacc, hipStream_t st)
+                          hipStream_t st)
 {
     if (bf16_in) {
         switch (d) {
-            case 64: return pre_t<bf16, 64>(O, dO, BH, N, Dd, dQacc, st);
-            case 80: return pre_t<bf16, 80>(O, dO, BH, N, Dd, dQacc, st);
-            case 128: return pre_t<bf16, 128>(O, dO, BH, N, Dd, dQacc, st);
+            case 64: return pre_t<bf16, 64>(O, dO, BH, N, Dd, st);
+            case 80: return pre_t<bf16, 80>(O, dO, BH, N, Dd, st);
+            case 128: return pre_t<bf16, 128>(O, dO, BH, N, Dd, st);
         }
     } else {
         switch (d) {
-            case 64: return pre_t<float, 64>(O, dO, BH, N, Dd, dQacc, st);
-            case 80: return pre_t<float, 80>(O, dO, BH, N, Dd, dQacc, st);
-            case 128: return pre_t<float, 128>(O, dO, BH, N, Dd, dQacc, st);
+            case 64: return pre_t<float, 64>(O, dO, BH, N, Dd, st);
+            case 80: return pre_t<float, 80>(O, dO, BH, N, Dd, st);
+            case 128: return pre_t<float, 128>(O, dO, BH, N, Dd, st);
         }
     }
     return hipErrorInvalidValue;
 }
 
-template <typename T, int D, bool CAUSAL, typename G>
-static hipError_t main_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                         const float* Dd, int BH, int N, float scale, float* dQacc, void* dK, void* dV,
-                         hipStream_t st)
+template <int D, bool CAUSAL, typename G>
+static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                         const float* Dd, int BH, int N, float scale, void* dK, void* dV, hipStream_t st)
 {
-    if constexpr (sizeof(T) == 2) {
-        using C = BwdBf16Cfg<D>;
-        const int nkblk = (N + C::BN - 1) / C::BN;
-        hipLaunchKernelGGL((bwd_kernel_bf16<D, CAUSAL, G>), dim3(nkblk * BH), dim3(256), 0, st,
-                           (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, dQacc,
-                           (G*)dK, (G*)dV, N, nkblk, scale);
-    } else {
-        using C = BwdCfg<T, D>;
-        const int nkblk = (N + C::BN - 1) / C::BN;
-        hipLaunchKernelGGL((bwd_kernel<T, D, CAUSAL, G>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
-                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, LSE, Dd, dQacc, (G*)dK,
-                           (G*)dV, N, nkblk, scale);
-    }
+    const int nkblk = (N + BwdKVCfg<D>::BN - 1) / BwdKVCfg<D>::BN;
+    hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G>), dim3(nkblk * BH), dim3(256), 0, st, (const bf16*)Q,
+                       (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale);
     return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t main_d(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                         const float* Dd, int BH, int N, float scale, int causal, float* dQacc, void* dK,
-                         void* dV, bool bf16_grad, hipStream_t st)
+template <int D, bool CAUSAL, typename G>
+static hipError_t dq_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                       const float* Dd, int BH, int N, float scale, void* dQ, hipStream_t st)
 {
-    if (causal) {
-        if (bf16_grad) return main_t<T, D, true, bf16>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
-        return main_t<T, D, true, float>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
-    }
-    if (bf16_grad) return main_t<T, D, false, bf16>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
-    return main_t<T, D, false, float>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+    const int nqblk = (N + BwdQCfg<D>::BM - 1) / BwdQCfg<D>::BM;
+    hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
+                       (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale);
+    return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                           const float* Dd, bool bf16_in, int BH, int N, int d, float scale, int causal,
-                           float* dQacc, void* dK, void* dV, bool bf16_grad, hipStream_t st)
+#define ATTN_DISPATCH_D_CAUSAL_G(FN, ...)                                                        \
+    switch (d) {                                                                                 \
+        case 64:                                                                                 \
+            if (causal) return bf16_grad ? FN<64, true, bf16>(__VA_ARGS__) : FN<64, true, float>(__VA_ARGS__);    \
+            return bf16_grad ? FN<64, false, bf16>(__VA_ARGS__) : FN<64, false, float>(__VA_ARGS__);             \
+        case 80:                                                                                 \
+            if (causal) return bf16_grad ? FN<80, true, bf16>(__VA_ARGS__) : FN<80, true, float>(__VA_ARGS__);    \
+            return bf16_grad ? FN<80, false, bf16>(__VA_ARGS__) : FN<80, false, float>(__VA_ARGS__);             \
+        case 128:                                                                                \
+            if (causal) return bf16_grad ? FN<128, true, bf16>(__VA_ARGS__) : FN<128, true, float>(__VA_ARGS__);  \
+            return bf16_grad ? FN<128, false, bf16>(__VA_ARGS__) : FN<128, false, float>(__VA_ARGS__);           \
+    }                                                                                            \
+    return hipErrorInvalidValue;
+
+hipError_t launch_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                           const float* Dd, int BH, int N, int d, float scale, int causal, void* dK, void* dV,
+                           bool bf16_grad, hipStream_t st)
 {
-    if (bf16_in) {
-        switch (d) {
-            case 64: return main_d<bf16, 64>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
-            case 80: return main_d<bf16, 80>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
-            case 128: return main_d<bf16, 128>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
-        }
-    } else {
-        switch (d) {
-            case 64: return main_d<float, 64>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
-            case 80: return main_d<float, 80>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
-            case 128: return main_d<float, 128>(Q, K, V, dO, LSE, Dd, BH, N, scale, causal, dQacc, dK, dV, bf16_grad, st);
-        }
+    ATTN_DISPATCH_D_CAUSAL_G(dkdv_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dK, dV, st)
+}
+
+hipError_t launch_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                         const float* Dd, int BH, int N, int d, float scale, int causal, void* dQ, bool bf16_grad,
+                         hipStream_t st)
+{
+    ATTN_DISPATCH_D_CAUSAL_G(dq_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dQ, st)
+}
+
+template <int D, bool CAUSAL>
+static hipError_t f32_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                        const float* Dd, int BH, int N, float scale, float* dQacc, float* dK, float* dV,
+                        hipStream_t st)
+{
+    using C = BwdCfg<float, D>;
+    const long n4 = (long)BH * N * D / 4;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dQacc, n4);
+    const int nkblk = (N + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL((bwd_kernel<float, D, CAUSAL, float>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
+                       (const float*)Q, (const float*)K, (const float*)V, (const float*)dO, LSE, Dd, dQacc, dK,
+                       dV, N, nkblk, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                          const float* Dd, int BH, int N, int d, float scale, int causal, float* dQacc, float* dK,
+                          float* dV, hipStream_t st)
+{
+    switch (d) {
+        case 64: return causal ? f32_t<64, true>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st)
+                               : f32_t<64, false>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+        case 80: return causal ? f32_t<80, true>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st)
+                               : f32_t<80, false>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+        case 128: return causal ? f32_t<128, true>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st)
+                                : f32_t<128, false>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
     }
     return hipErrorInvalidValue;
 }

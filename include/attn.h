@@ -65,33 +65,49 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, attn_dtype dt,
                      int B, int H, int N, int d, float scale, int causal,
                      void* O, float* LSE, void* stream);
 
-/* Backward preprocess: D_i = sum_k dO_ik O_ik in fp32 (the row-wise inner
- * product the corrected dS formula needs), and dQacc = 0.  O, dO: dtype `dt`.
- * D: fp32 [B,H,N] output.  dQacc: fp32 [B,H,N,d] output, zero-filled. */
+/* Backward preprocess: D_i = sum_k dO_ik O_ik in fp32, the row-wise inner
+ * product the corrected dS formula needs (D_i = sum_j P_ij dP_ij).  O, dO:
+ * dtype `dt`.  D: fp32 [B,H,N] output. */
 attn_status attn_bwd_preprocess(const void* O, const void* dO, attn_dtype dt,
-                                int B, int H, int N, int d,
-                                float* D, float* dQacc, void* stream);
+                                int B, int H, int N, int d, float* D, void* stream);
 
-/* Backward main pass: one workgroup per block of keys; recomputes S and P
- * from Q, K and the saved LSE ("Recomputation", '[LLM] Flash Attention' blog;
- * FlashAttention-2 review, section 2 (3)), writes dK and dV (fp32) once and
- * adds dQ into dQacc (fp32, must hold zeros or a partial sum) with atomics.
- * D must come from attn_bwd_preprocess with the same O and dO. */
+/* Backward, key side: dK and dV (fp32 outputs, written once).  One workgroup per
+ * block of keys recomputes S and P from Q, K and the saved LSE
+ * ("Recomputation", '[LLM] Flash Attention' blog; FlashAttention-2 review,
+ * 'core algorithm' answer, section 2 (3)) and reduces dV = P^T dO and
+ * dK = scale dS^T Q on chip.  D from attn_bwd_preprocess; LSE from attn_fwd with
+ * the same scale and causal flag.  dt must be ATTN_BF16 (else ATTN_EUNSUPPORTED;
+ * attn_bwd_main covers fp32 inputs). */
+attn_status attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                          const float* LSE, const float* D, attn_dtype dt,
+                          int B, int H, int N, int d, float scale, int causal,
+                          float* dK, float* dV, void* stream);
+
+/* Backward, query side: dQ = scale dS K (fp32 output, written once, no
+ * atomics).  One workgroup per block of queries recomputes S^T, P^T and dS^T.
+ * Same arguments and restrictions as attn_bwd_dkdv. */
+attn_status attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
+                        const float* LSE, const float* D, attn_dtype dt,
+                        int B, int H, int N, int d, float scale, int causal,
+                        float* dQ, void* stream);
+
+/* Backward after the preprocess: dQ, dK, dV (fp32, written once).  bf16 inputs:
+ * attn_bwd_dkdv then attn_bwd_dq.  fp32 inputs: one kernel for all three, with
+ * dQ accumulated by fp32 atomics into dQ after zero-filling it. */
 attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const void* dO,
                           const float* LSE, const float* D, attn_dtype dt,
                           int B, int H, int N, int d, float scale, int causal,
-                          float* dQacc, float* dK, float* dV, void* stream);
+                          float* dQ, float* dK, float* dV, void* stream);
 
-/* Bytes of device workspace attn_bwd needs: D (B*H*N fp32) rounded up to
- * 256 bytes, plus the fp32 dQ accumulator (B*H*N*d fp32) when grad_dt is
- * ATTN_BF16.  Returns 0 for invalid sizes. */
-size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype grad_dt);
+/* Bytes of device workspace attn_bwd needs: D (B*H*N fp32) rounded up to 256
+ * bytes.  Returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
-/* Full backward = attn_bwd_preprocess + attn_bwd_main (+ a conversion of the
- * fp32 accumulators to bf16 when grad_dt = ATTN_BF16).  Q, K, V, O, dO: dtype
+/* Full backward = attn_bwd_preprocess + attn_bwd_main.  Q, K, V, O, dO: dtype
  * `dt`; LSE from attn_fwd with the same scale and causal flag.  dQ, dK, dV:
- * outputs of dtype grad_dt.  workspace: device, 16-byte aligned, at least
- * attn_bwd_workspace_bytes(B, H, N, d, grad_dt) bytes (else ATTN_EINVAL). */
+ * outputs of dtype grad_dt (ATTN_BF16 gradients need bf16 inputs, else
+ * ATTN_EUNSUPPORTED).  workspace: device, 16-byte aligned, at least
+ * attn_bwd_workspace_bytes(B, H, N, d) bytes (else ATTN_EINVAL). */
 attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                      const void* dO, const float* LSE, attn_dtype dt,
                      int B, int H, int N, int d, float scale, int causal,

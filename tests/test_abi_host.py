@@ -60,26 +60,29 @@ def test_fwd_rejects_before_launch(kw, expect):
 
 def test_bwd_rejects_before_launch():
     L = attn.lib()
-    ws = L.attn_bwd_workspace_bytes(1, 1, 16, 64, attn.ATTN_F32)
+    ws = L.attn_bwd_workspace_bytes(1, 1, 16, 64)
     assert ws == 256
-    args = lambda d=64, wsb=ws, g=attn.ATTN_F32, w=P: (P, P, P, P, P, P, attn.ATTN_BF16, 1, 1, 16, d, 0.125, 1,
-                                                      P, P, P, g, w, ctypes.c_size_t(wsb), None)
+    args = lambda d=64, wsb=ws, g=attn.ATTN_F32, w=P, dt=attn.ATTN_BF16: (
+        P, P, P, P, P, P, dt, 1, 1, 16, d, 0.125, 1, P, P, P, g, w, ctypes.c_size_t(wsb), None)
     assert L.attn_bwd(*args(wsb=ws - 1)) == attn.ATTN_EINVAL
     assert L.attn_bwd(*args(d=100)) == attn.ATTN_EUNSUPPORTED
     assert L.attn_bwd(*args(g=5)) == attn.ATTN_EINVAL
     assert L.attn_bwd(*args(w=NUL)) == attn.ATTN_EINVAL
+    assert L.attn_bwd(*args(dt=attn.ATTN_F32, g=attn.ATTN_BF16)) == attn.ATTN_EUNSUPPORTED
     assert L.attn_bwd_main(P, P, P, P, P, P, 1, 1, 1, 16, 64, math.nan, 0, P, P, P, None) == attn.ATTN_EINVAL
-    assert L.attn_bwd_preprocess(P, MIS, 1, 1, 1, 16, 64, P, P, None) == attn.ATTN_EINVAL
+    assert L.attn_bwd_preprocess(P, MIS, 1, 1, 1, 16, 64, P, None) == attn.ATTN_EINVAL
+    # the split key-side / query-side passes exist for bf16 inputs only
+    assert L.attn_bwd_dkdv(P, P, P, P, P, P, attn.ATTN_F32, 1, 1, 16, 64, 0.1, 0, P, P, None) == attn.ATTN_EUNSUPPORTED
+    assert L.attn_bwd_dq(P, P, P, P, P, P, attn.ATTN_F32, 1, 1, 16, 64, 0.1, 0, P, None) == attn.ATTN_EUNSUPPORTED
+    assert L.attn_bwd_dq(P, P, P, P, P, NUL, attn.ATTN_BF16, 1, 1, 16, 64, 0.1, 0, P, None) == attn.ATTN_EINVAL
 
 
 def test_workspace_sizes():
     L = attn.lib()
     rows = 4 * 16 * 4096
-    f32 = L.attn_bwd_workspace_bytes(4, 16, 4096, 128, attn.ATTN_F32)
-    bf = L.attn_bwd_workspace_bytes(4, 16, 4096, 128, attn.ATTN_BF16)
-    assert f32 == rows * 4
-    assert bf == rows * 4 + rows * 128 * 4
-    assert L.attn_bwd_workspace_bytes(0, 16, 4096, 128, attn.ATTN_F32) == 0
+    assert L.attn_bwd_workspace_bytes(4, 16, 4096, 128) == rows * 4
+    assert L.attn_bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert L.attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
 
 
 def test_status_strings():
