@@ -373,6 +373,203 @@ __global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q,
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 forward (the hot path).  Same per-lane softmax as above; K and V tiles go
+// straight from HBM/L2 into swizzled LDS rows (direct-to-LDS loads, no staging
+// registers, no transposing stores) and V^T reaches the MFMA through transpose
+// reads.  sK0/sK1/sV0/sV1 are separate __shared__ objects and the loop is
+// unrolled by two, so the compiler can tell the next tile's in-flight loads from
+// the current tile's reads.  Two workgroups per CU (<= 256 registers per wave).
+// ----------------------------------------------------------------------------
+template <int D>
+struct FwdBf16Cfg {
+    static constexpr int BM = 128, BN = 64, NKT = BN / 32;
+    static constexpr int RB = D == 64 ? 128 : 256;
+    static constexpr int DP = (D + 31) / 32 * 32, NDT = DP / 32;
+    static constexpr int NKS = D / 16;
+    static constexpr int T_BYTES = BN * RB;
+    static_assert(4 * T_BYTES <= 80 * 1024, "two workgroups per CU");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                                          const bf16* __restrict__ V, bf16* __restrict__ O,
+                                                          float* __restrict__ LSE, int N, int nqblk, float c,
+                                                          int negate_q)
+{
+    using C = FwdBf16Cfg<D>;
+    constexpr int RB = C::RB;
+    constexpr uint32_t ROWB = D * 2;
+    constexpr float NEG_INF = -__builtin_inff();
+    __shared__ __attribute__((aligned(1024))) char sK0[C::T_BYTES], sK1[C::T_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sV0[C::T_BYTES], sV1[C::T_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = bid / nqblk;
+    int qb = bid - head * nqblk;
+    if (CAUSAL) qb = nqblk - 1 - qb;                 // heavy row blocks first
+    const int q0 = qb * C::BM;
+    const int q0w = q0 + 32 * wave;
+    const int myq = q0w + l32;
+    const size_t hoff = (size_t)head * (size_t)N * D;
+    const bf16* __restrict__ Kh = K + hoff;
+    const bf16* __restrict__ Vh = V + hoff;
+    TileLane<RB, C::NKS> tl;
+    tl.init(lane);
+
+    // Q fragments (B operand of S^T = K Q^T), sign-flipped for a negative scale
+    bf16x8 qf[C::NKS];
+    {
+        const auto rq = make_rsrc(Q + hoff, (uint32_t)N * ROWB);
+        const uint32_t ro = (uint32_t)myq * ROWB + 16 * h;
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+            u32x4 raw = buf_ld16(rq, ro + 32 * s);
+            if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            qf[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    f32x16 oacc[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+    float mc = NEG_INF, l = 0.f;
+
+    const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+    const int ntiles = (kv_end + C::BN - 1) / C::BN;
+
+    auto issue_tile = [&](int j, char* sK, char* sV) {
+        const int kv0 = j * C::BN;
+        const uint32_t bytes = (uint32_t)(N - kv0) * ROWB;        // rows past N read as zeros
+        dma_rows<D, RB>(make_rsrc(Kh + (size_t)kv0 * D, bytes), sK, wave * (C::BN / 4), C::BN / 4, lane);
+        dma_rows<D, RB>(make_rsrc(Vh + (size_t)kv0 * D, bytes), sV, wave * (C::BN / 4), C::BN / 4, lane);
+    };
+
+    auto tile_body = [&](int j, const char* sK, const char* sV) {
+        const int kv0 = j * C::BN;
+        f32x16 sacc[C::NKT];
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt)
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sK, 32 * kt, s), qf[s], sacc[kt], 0, 0, 0);
+
+        // lane: query myq, keys kv0 + 32 kt + 8 (r/4) + 4 h + r%4
+        const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > q0w) || (kv0 + C::BN > N);
+        if (need_mask) {
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if ((CAUSAL && key > myq) || key >= N) sacc[kt][r] = NEG_INF;
+                }
+        }
+        float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx4[r >> 2] = max3f(mx4[r >> 2], sacc[kt][r], sacc[kt][r + 1]);
+        float mx = max3f(mx4[0], mx4[1], fmaxf(mx4[2], mx4[3]));
+        mx = fmaxf(mx, xor32(mx));
+        const float mxc = (mx == NEG_INF) ? NEG_INF : mx * c;
+        // the reference max moves only when the tile's max exceeds it by 2^kLazyLog2
+        if (__builtin_amdgcn_ballot_w64(mxc > mc + kLazyLog2) != 0) {
+            const float mnew = fmaxf(mc, mxc);
+            const float alpha = fast_exp2(mc - mnew);           // 0 on the first tile
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            mc = mnew;
+        }
+        if (need_mask) {
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float sv = sacc[kt][r];
+                    sacc[kt][r] = (sv == NEG_INF) ? 0.f : fast_exp2(fmaf(sv, c, -mc));
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kt][r] = fast_exp2(fmaf(sacc[kt][r], c, -mc));
+        }
+        // P in bf16; the row sum is taken over exactly these values
+        bf16x8 pf[C::NKT][2];
+        float ls[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[kt][s2][e] = to_bf16(sacc[kt][8 * s2 + e]);
+                const u32x4 w = __builtin_bit_cast(u32x4, pf[kt][s2]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) ls[s2] = sum2_bf16(w[x], ls[s2]);
+            }
+        l += ls[0] + ls[1];
+        // O^T += V^T P^T
+#pragma unroll
+        for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt)
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sV, 32 * kt + 16 * s2, dt), pf[kt][s2],
+                                                                       oacc[dt], 0, 0, 0);
+    };
+
+    auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
+        wait_vmem_all();                                // this wave's loads of tile j landed
+        __syncthreads();                                // everyone's; tile j-1 fully read
+        if (j + 1 < ntiles) issue_tile(j + 1, kn, vn);
+        if (!(CAUSAL && j * C::BN > q0w + 31))          // else every key follows this wave's rows
+            tile_body(j, kc, vc);
+    };
+
+    issue_tile(0, sK0, sV0);
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+        step(j, sK0, sV0, sK1, sV1);
+        step(j + 1, sK1, sV1, sK0, sV0);
+    }
+    if (j < ntiles) step(j, sK0, sV0, sK1, sV1);
+
+    // epilogue: one division by l, O and LSE written once
+    const float lt = l + xor32(l);
+    const float inv = 1.0f / lt;
+    if (myq < N) {
+        bf16* dst = O + hoff + (size_t)myq * D;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * dt + 8 * g + 4 * h;
+                if (d0 < D) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = to_bf16(oacc[dt][4 * g + e] * inv);
+                    *reinterpret_cast<bf16x4*>(dst + d0) = v;
+                }
+            }
+        if (h == 0) LSE[(size_t)head * N + myq] = (mc + __log2f(lt)) * kLn2;
+    }
+}
+
 template <typename T, int D, bool CAUSAL, int QT, int MINW>
 static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int BH, int N, float scale, hipStream_t st)
@@ -386,26 +583,28 @@ static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void
     return hipGetLastError();
 }
 
-// Tile table.  bf16: one 32-row query tile per wave and two workgroups per CU
-// (<= 256 registers per wave), so that one wave's softmax runs on the VALU
-// while the other wave of the same SIMD keeps the matrix cores busy.
-// fp32 (fragments four times larger per contraction step): one workgroup per CU.
-#ifndef ATTN_FWD_BF16_QT
-#define ATTN_FWD_BF16_QT 1
-#endif
-#ifndef ATTN_FWD_BF16_MINW
-#define ATTN_FWD_BF16_MINW 2
-#endif
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
+                                  float scale, hipStream_t st)
+{
+    const int nqblk = (N + FwdBf16Cfg<D>::BM - 1) / FwdBf16Cfg<D>::BM;
+    hipLaunchKernelGGL((fwd_kernel_bf16<D, CAUSAL>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
+                       (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk, fabsf(scale) * kLog2e,
+                       (int)(scale < 0.f));
+    return hipGetLastError();
+}
 
 template <typename T, int D>
 static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                int BH, int N, float scale, int causal, hipStream_t st)
 {
-    constexpr bool isbf = sizeof(T) == 2;
-    constexpr int QT = isbf ? ATTN_FWD_BF16_QT : 1;
-    constexpr int MINW = isbf ? ATTN_FWD_BF16_MINW : 1;
-    if (causal) return launch_fwd_t<T, D, true, QT, MINW>(Q, K, V, O, LSE, BH, N, scale, st);
-    return launch_fwd_t<T, D, false, QT, MINW>(Q, K, V, O, LSE, BH, N, scale, st);
+    if constexpr (sizeof(T) == 2) {
+        if (causal) return launch_fwd_bf16<D, true>(Q, K, V, O, LSE, BH, N, scale, st);
+        return launch_fwd_bf16<D, false>(Q, K, V, O, LSE, BH, N, scale, st);
+    } else {
+        if (causal) return launch_fwd_t<T, D, true, 1, 1>(Q, K, V, O, LSE, BH, N, scale, st);
+        return launch_fwd_t<T, D, false, 1, 1>(Q, K, V, O, LSE, BH, N, scale, st);
+    }
 }
 
 hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, bool bf16_in,
