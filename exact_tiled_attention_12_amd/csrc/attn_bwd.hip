@@ -482,7 +482,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     const bf16* __restrict__ Qh = Q + hoff;
     const bf16* __restrict__ dOh = dO + hoff;
     const float c2 = scale * kLog2e;
-    TileLane<RB, C::NKS> tl;
+    TileLane<RB, C::NKS, C::NDT, false> tl;
     tl.init(lane);
 
     // resident V fragments (B operand of dP = dO V^T); K rows to LDS (B operand of S)
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
 #pragma unroll
         for (int s = 0; s < C::NKS; ++s) vf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rv, ro + 32 * s));
     }
-    dma_rows<D, RB>(make_rsrc(K + hoff + (size_t)k0 * D, (uint32_t)(N - k0) * ROWB), sK, wave * (C::BN / 4),
+    dma_rows<D, RB, false>(make_rsrc(K + hoff + (size_t)k0 * D, (uint32_t)(N - k0) * ROWB), sK, wave * (C::BN / 4),
                     C::BN / 4, lane);
 
     f32x16 dvacc[C::NDT], dkacc[C::NDT];
@@ -509,8 +509,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     auto issue_block = [&](int i, char* sQ, char* sG) {
         const int q0 = i * C::BM;
         const uint32_t bytes = (uint32_t)(N - q0) * ROWB;         // rows past N read as zeros
-        dma_rows<D, RB>(make_rsrc(Qh + (size_t)q0 * D, bytes), sQ, wave * (C::BM / 4), C::BM / 4, lane);
-        dma_rows<D, RB>(make_rsrc(dOh + (size_t)q0 * D, bytes), sG, wave * (C::BM / 4), C::BM / 4, lane);
+        dma_rows<D, RB, false>(make_rsrc(Qh + (size_t)q0 * D, bytes), sQ, wave * (C::BM / 4), C::BM / 4, lane);
+        dma_rows<D, RB, false>(make_rsrc(dOh + (size_t)q0 * D, bytes), sG, wave * (C::BM / 4), C::BM / 4, lane);
         if (wave == 0)
             lreg = -kLog2e * buf_ld4f(make_rsrc(LSE + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
         if (wave == 1) lreg = buf_ld4f(make_rsrc(Dg + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
     const bf16* __restrict__ Kh = K + hoff;
     const bf16* __restrict__ Vh = V + hoff;
     const float c2 = scale * kLog2e;
-    TileLane<RB, C::NKS> tl;
+    TileLane<RB, C::NKS, C::NDT, true> tl;
     tl.init(lane);
 
     // Q and dO fragments (B operands), this lane's -LSE*log2e and D
@@ -694,8 +694,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
     auto issue_tile = [&](int j, char* sK, char* sV) {
         const int kv0 = j * C::BN;
         const uint32_t bytes = (uint32_t)(N - kv0) * ROWB;        // rows past N read as zeros
-        dma_rows<D, RB>(make_rsrc(Kh + (size_t)kv0 * D, bytes), sK, wave * (C::BN / 4), C::BN / 4, lane);
-        dma_rows<D, RB>(make_rsrc(Vh + (size_t)kv0 * D, bytes), sV, wave * (C::BN / 4), C::BN / 4, lane);
+        dma_rows<D, RB, true>(make_rsrc(Kh + (size_t)kv0 * D, bytes), sK, wave * (C::BN / 4), C::BN / 4, lane);
+        dma_rows<D, RB, true>(make_rsrc(Vh + (size_t)kv0 * D, bytes), sV, wave * (C::BN / 4), C::BN / 4, lane);
     };
 
     auto tile_body = [&](int j, const char* sK, const char* sV) {

@@ -76,26 +76,72 @@ __device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off
 
 // ---- LDS tiles written by direct-to-LDS loads (no padding possible) ----
 // Rows of RB = 256 bytes (16 slots of 16 B) or 128 bytes (8 slots).  Logical
-// 16-byte chunk c of row r lives in slot swz(r, c).  The XOR masks are chosen so
-// that (a) 16 lanes reading the same chunk of 16 consecutive rows and (b) the
-// transpose-read pattern (4 consecutive rows x 2 adjacent chunks per 16 lanes)
-// both hit distinct bank groups.
-template <int RB>
+// 16-byte chunk c of row r lives in slot swz(r, c).  Measured on gfx950 (64 banks;
+// 16 lanes per cycle for 16-byte reads, 32 lanes for the 8-byte transpose reads),
+// the layouts below make both access patterns conflict-free:
+//   (a) 16 lanes reading the same chunk of 16 consecutive rows (row fragments);
+//   (b) 32 lanes reading 4 consecutive rows x 4 adjacent chunks (transpose reads).
+// 256-byte rows: slot = pi(c) ^ f(r), where pi sends chunk bit 1 to slot bit 3 (so
+// the two 16-lane halves of (b) use opposite bank halves) and f is a permutation
+// of the row's low four bits.  128-byte rows: slot = c ^ g(r / 2), g flips slot
+// bit 2 between even and odd row pairs.
+__device__ __forceinline__ int swz_pi(int c)
+{
+    return (c & 1) | (((c >> 1) & 1) << 3) | (((c >> 2) & 1) << 1) | (((c >> 3) & 1) << 2);
+}
+__device__ __forceinline__ int swz_pi_inv(int s)
+{
+    return (s & 1) | (((s >> 3) & 1) << 1) | (((s >> 1) & 1) << 2) | (((s >> 2) & 1) << 3);
+}
+__device__ __forceinline__ int swz_f(int r)
+{
+    return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (r & 8);
+}
+__device__ __forceinline__ int swz_g(int r)
+{
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | ((x >> 1) & 3);
+}
+//
+// A second, XOR-only layout (FAST = false) is conflict-free for (a) and for each
+// 16-lane half of (b) but not for (b) as a whole.  Its offsets for the four
+// 32-column tiles and for the second transpose read are constant distances from
+// two per-lane values, which saves registers and address arithmetic; the kernel
+// that runs one wave per SIMD (nothing to hide extra VALU work) uses it.
+__device__ __forceinline__ int swz_x256(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8); }
+__device__ __forceinline__ int swz_x128(int r)
+{
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+}
+template <int RB, bool FAST>
 __device__ __forceinline__ int swz(int r, int c)
 {
-    if constexpr (RB == 256) {
-        return c ^ (((r & 3) << 1) | ((r >> 2) & 1) | (r & 8));
+    if constexpr (FAST) {
+        if constexpr (RB == 256) return swz_pi(c) ^ swz_f(r);
+        else return c ^ swz_g(r);
     } else {
-        const int x = (r >> 1) & 7;
-        return c ^ (((x & 1) << 1) | ((x >> 1) & 1) | (x & 4));
+        if constexpr (RB == 256) return c ^ swz_x256(r);
+        else return c ^ swz_x128(r);
+    }
+}
+// the chunk stored in slot `slot` of row r
+template <int RB, bool FAST>
+__device__ __forceinline__ int swz_chunk(int r, int slot)
+{
+    if constexpr (FAST) {
+        if constexpr (RB == 256) return swz_pi_inv(slot ^ swz_f(r));
+        else return slot ^ swz_g(r);
+    } else {
+        return swz<RB, false>(r, slot);      // XOR: an involution
     }
 }
 
 // Byte offset of bf16 element (r, col) inside an RB-row tile.
-template <int RB>
+template <int RB, bool FAST>
 __device__ __forceinline__ int tile_off(int r, int col)
 {
-    return r * RB + swz<RB>(r, col >> 3) * 16 + (col & 7) * 2;
+    return r * RB + swz<RB, FAST>(r, col >> 3) * 16 + (col & 7) * 2;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -110,40 +156,16 @@ __device__ __forceinline__ u32x2 lds_tr16(const char* p)
     return __builtin_bit_cast(u32x2, v);
 }
 
-// MFMA operand fragment (8 bf16) for a lane that needs X[k][m] with
-// m = m0 + lane % 32 and k = k0 + 8*(e/4) + 4*(lane/32) + e%4, e = 0..7, read
-// from a row-major (k rows, m columns) bf16 tile in LDS: two transpose reads.
-template <int RB>
-__device__ __forceinline__ bf16x8 ld_frag_tr(const char* tile, int k0, int m0, int lane)
-{
-    const int g = lane >> 4, j = lane & 15;
-    const int row = k0 + 4 * (g >> 1) + (j >> 2);
-    const int col = m0 + 16 * (g & 1) + 4 * (j & 3);
-    const u32x2 a = lds_tr16(tile + tile_off<RB>(row, col));
-    const u32x2 b = lds_tr16(tile + tile_off<RB>(row + 8, col));
-    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-}
-
-// MFMA operand fragment (8 bf16) for a lane that needs X[m][k] with
-// m = m0 + lane % 32 and k = k0 + 8*(lane/32) .. +7: one 16-byte row read.
-template <int RB>
-__device__ __forceinline__ bf16x8 ld_frag_row(const char* tile, int m0, int k0, int lane)
-{
-    const int row = m0 + (lane & 31);
-    const int c = (k0 >> 3) + (lane >> 5);
-    return __builtin_bit_cast(bf16x8, ld16(tile + row * RB + swz<RB>(row, c) * 16));
-}
-
 // Direct-to-LDS copy of `rows` rows of a bf16 [*, D] array into an RB-row tile
 // (swizzled), by one wave: each instruction moves 1 KB.  `r` covers the source
 // rows (rows past its end read as zeros); chunks past D are filled with zeros.
-template <int D, int RB>
+template <int D, int RB, bool FAST>
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, char* tile, int row0, int rows, int lane)
 {
     constexpr int SLOTS = RB / 16, ROWS_PER = 1024 / RB, CPR = D / 8;
     for (int base = row0; base < row0 + rows; base += ROWS_PER) {
         const int row = base + lane / SLOTS;
-        const int c = swz<RB>(row, lane % SLOTS);             // swz is an involution in c
+        const int c = swz_chunk<RB, FAST>(row, lane % SLOTS);
         const uint32_t off = c < CPR ? (uint32_t)(row * D * 2 + c * 16) : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(tile + base * RB),
                                                  16, off, 0, 0, 0);
@@ -151,26 +173,38 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, char* tile, i
 }
 
 // Per-lane byte offsets into RB-row swizzled tiles, computed once, so that every
-// fragment read in a loop is (lane offset) + (compile-time constant).
-//   row(m0, s): ld_frag_row(tile, m0, 16 s) for m0 a multiple of 16
-//   tr(k0, j):  ld_frag_tr(tile, k0, 32 j) for k0 a multiple of 16; the second of
-//               the two transpose reads sits at a constant distance from the first.
-template <int RB, int NKS>
+// fragment read in a loop is (lane offset) + (compile-time constant).  The swizzle
+// depends only on a row's low four bits, so moving by a multiple of 16 rows is a
+// constant offset.
+//   row(tile, m0, s): 16-byte row read, rows m0 + lane%32, chunk 2 s + lane/32
+//   tr(tile, k0, jt): the MFMA operand fragment (8 bf16) for a lane that needs
+//     X[k][m] with m = 32 jt + lane%32 and k = k0 + 8 (e/4) + 4 (lane/32) + e%4,
+//     e = 0..7, from a row-major (k rows, m columns) tile: two transpose reads.
+//     Within each group of 16 lanes, ds_read_b64_tr_b16 hands lane i element i%4
+//     of the reads of lanes 4k + i/4 (k = 0..3), so lane 16g + j reads row
+//     k0 + 4 (g/2) + j/4, columns 32 jt + 16 (g%2) + 4 (j%4) .. +3.
+template <int RB, int NKS, int NJT, bool FAST>
 struct TileLane {
     int ro[NKS];
-    int tr0, tr1;
+    int ta[FAST ? NJT : 2], tb[FAST ? NJT : 1];
     __device__ __forceinline__ void init(int lane)
     {
         const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) ro[s] = l32 * RB + swz<RB>(l32, 2 * s + h) * 16;
+        for (int s = 0; s < NKS; ++s) ro[s] = l32 * RB + swz<RB, FAST>(l32, 2 * s + h) * 16;
         const int g = lane >> 4, j = lane & 15;
         const int rl = 4 * (g >> 1) + (j >> 2);            // row within the 8-row group
         const int cl = 16 * (g & 1) + 4 * (j & 3);         // column within the 32-column tile
-        const int T = swz<RB>(rl, cl >> 3);                // slot for column tile 0
-        tr0 = rl * RB + T * 16 + ((cl >> 2) & 1) * 8;
-        if constexpr (RB == 256) tr1 = rl * RB + (T ^ 4) * 16 + ((cl >> 2) & 1) * 8;
-        else tr1 = tr0;
+        if constexpr (FAST) {
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt) {
+                ta[jt] = tile_off<RB, FAST>(rl, 32 * jt + cl);
+                tb[jt] = tile_off<RB, FAST>(rl + 8, 32 * jt + cl);
+            }
+        } else {
+            ta[0] = tile_off<RB, FAST>(rl, cl);
+            ta[1] = tile_off<RB, FAST>(rl, 32 + cl);
+        }
     }
     __device__ __forceinline__ bf16x8 row(const char* tile, int m0, int s) const
     {
@@ -179,11 +213,16 @@ struct TileLane {
     __device__ __forceinline__ bf16x8 tr(const char* tile, int k0, int jt) const
     {
         int o, o2;
-        if constexpr (RB == 256) {
-            o = k0 * RB + ((jt & 2) ? 128 : 0) + ((jt & 1) ? tr1 : tr0);
+        if constexpr (FAST) {
+            o = k0 * RB + ta[jt];
+            o2 = k0 * RB + tb[jt];
+        } else if constexpr (RB == 256) {
+            // column tile jt: slot = (4 jt) ^ T, i.e. +128 B for jt >= 2 and tile parity via ta[jt & 1];
+            // row + 8 flips slot bit 3: +/-128 B
+            o = k0 * RB + ((jt & 2) ? 128 : 0) + ta[jt & 1];
             o2 = o + 8 * RB + ((jt & 2) ? -128 : 128);
         } else {
-            o = k0 * RB + (jt ? 64 : 0) + tr0;
+            o = k0 * RB + ta[jt & 1];
             o2 = o + 8 * RB + (jt ? -64 : 64);
         }
         const u32x2 a = lds_tr16(tile + o);

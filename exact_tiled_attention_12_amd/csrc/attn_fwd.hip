@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
     const size_t hoff = (size_t)head * (size_t)N * D;
     const bf16* __restrict__ Kh = K + hoff;
     const bf16* __restrict__ Vh = V + hoff;
-    TileLane<RB, C::NKS> tl;
+    TileLane<RB, C::NKS, C::NDT, true> tl;
     tl.init(lane);
 
     // Q fragments (B operand of S^T = K Q^T), sign-flipped for a negative scale
@@ -447,8 +447,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
     auto issue_tile = [&](int j, char* sK, char* sV) {
         const int kv0 = j * C::BN;
         const uint32_t bytes = (uint32_t)(N - kv0) * ROWB;        // rows past N read as zeros
-        dma_rows<D, RB>(make_rsrc(Kh + (size_t)kv0 * D, bytes), sK, wave * (C::BN / 4), C::BN / 4, lane);
-        dma_rows<D, RB>(make_rsrc(Vh + (size_t)kv0 * D, bytes), sV, wave * (C::BN / 4), C::BN / 4, lane);
+        dma_rows<D, RB, true>(make_rsrc(Kh + (size_t)kv0 * D, bytes), sK, wave * (C::BN / 4), C::BN / 4, lane);
+        dma_rows<D, RB, true>(make_rsrc(Vh + (size_t)kv0 * D, bytes), sV, wave * (C::BN / 4), C::BN / 4, lane);
     };
 
     auto tile_body = [&](int j, const char* sK, const char* sV) {
