@@ -432,29 +432,36 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
 }
 
 // ----------------------------------------------------------------------------
-// bf16 backward, part 1: dK and dV.  One workgroup per BN = 128 keys (32 per
-// wave), iterating over query blocks of BM = 64 rows:
+// bf16 backward, part 1: dK and dV.  One workgroup of 8 waves per BN = 128 keys,
+// iterating over query blocks of BM = 64 rows.  Wave w owns the 32 keys of group
+// w % 4 and the 32 query rows w / 4 of each block, so two waves share every key
+// group and each keeps its own partial dK, dV (summed through LDS at the end).
+// That keeps a wave under 256 registers: two waves per SIMD, one's VALU work
+// overlapping the other's MFMAs.
 //   S = Q K^T, dP = dO V^T       (accumulator lane = one key, rows = queries)
 //   P = exp2(S c2 - LSE log2 e), dS = P o (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS   (contraction over queries; dO^T and Q^T
 //                                      come from transpose reads of row tiles)
 // LDS: sQ*/sG* hold the Q and dO rows of the current and next block (direct-to-LDS
-// loads into swizzled rows), sK the workgroup's K rows (row reads give the B
-// operand of S).  Separate __shared__ objects and a loop unrolled by two let the
-// compiler see that the in-flight loads never alias the tiles being read.
+// loads into swizzled rows); sK, sV the workgroup's K and V rows (row reads give
+// the B operands of S and dP).  Separate __shared__ objects and a loop unrolled by
+// two let the compiler see that the in-flight loads never alias the tiles read.
 // ----------------------------------------------------------------------------
 template <int D>
 struct BwdKVCfg {
-    static constexpr int BN = 128, BM = 64, NQT = BM / 32;
+    static constexpr int BN = 128, BM = 64, WAVES = 8;
     static constexpr int RB = D == 64 ? 128 : 256;        // LDS bytes per row
     static constexpr int DP = (D + 31) / 32 * 32, NDT = DP / 32;
     static constexpr int NKS = D / 16;
     static constexpr int Q_BYTES = BM * RB, K_BYTES = BN * RB;
-    static_assert(4 * Q_BYTES + K_BYTES + 4 * BM * 4 <= 160 * 1024, "LDS budget");
+    static_assert(4 * Q_BYTES + 2 * K_BYTES + 4 * BM * 4 <= 160 * 1024, "LDS budget");
+    // the end-of-kernel reduction parks one wave's dK (dV) partial, NDT*16 floats
+    // per lane, in a Q/dO buffer (a K/V tile holds two of them)
+    static_assert(NDT * 16 * 64 * 4 <= Q_BYTES, "dK partial fits a Q/dO buffer");
 };
 
 template <int D, bool CAUSAL, typename G>
-__global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+__global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE, const float* __restrict__ Dg,
                                                      G* __restrict__ dK, G* __restrict__ dV, int N, int nkblk,
@@ -465,18 +472,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     constexpr uint32_t ROWB = D * 2;                    // global bytes per row
     __shared__ __attribute__((aligned(1024))) char sQ0[C::Q_BYTES], sQ1[C::Q_BYTES];
     __shared__ __attribute__((aligned(1024))) char sG0[C::Q_BYTES], sG1[C::Q_BYTES];
-    __shared__ __attribute__((aligned(1024))) char sK[C::K_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sK[C::K_BYTES], sV[C::K_BYTES];
     __shared__ __attribute__((aligned(16))) float sL0[C::BM], sL1[C::BM], sD0[C::BM], sD1[C::BM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3, qh = wave >> 2;            // key group, query half
     const int l32 = lane & 31, h = lane >> 5;
 
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int head = bid / nkblk;
     const int kb = bid - head * nkblk;
     const int k0 = kb * C::BN;
-    const int k0w = k0 + 32 * wave;
+    const int k0w = k0 + 32 * kg;
     const int mykey = k0w + l32;
     const size_t hoff = (size_t)head * (size_t)N * D;
     const bf16* __restrict__ Qh = Q + hoff;
@@ -485,16 +493,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     TileLane<RB, C::NKS, C::NDT, false> tl;
     tl.init(lane);
 
-    // resident V fragments (B operand of dP = dO V^T); K rows to LDS (B operand of S)
-    bf16x8 vf[C::NKS];
+    // the workgroup's K and V rows to LDS (16 rows per wave each)
     {
-        const auto rv = make_rsrc(V + hoff, (uint32_t)N * ROWB);
-        const uint32_t ro = (uint32_t)mykey * ROWB + 16 * h;
-#pragma unroll
-        for (int s = 0; s < C::NKS; ++s) vf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rv, ro + 32 * s));
+        const uint32_t bytes = (uint32_t)(N - k0) * ROWB;
+        dma_rows<D, RB, false>(make_rsrc(K + hoff + (size_t)k0 * D, bytes), sK, wave * (C::BN / 8), C::BN / 8, lane);
+        dma_rows<D, RB, false>(make_rsrc(V + hoff + (size_t)k0 * D, bytes), sV, wave * (C::BN / 8), C::BN / 8, lane);
     }
-    dma_rows<D, RB, false>(make_rsrc(K + hoff + (size_t)k0 * D, (uint32_t)(N - k0) * ROWB), sK, wave * (C::BN / 4),
-                    C::BN / 4, lane);
 
     f32x16 dvacc[C::NDT], dkacc[C::NDT];
 #pragma unroll
@@ -509,8 +513,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     auto issue_block = [&](int i, char* sQ, char* sG) {
         const int q0 = i * C::BM;
         const uint32_t bytes = (uint32_t)(N - q0) * ROWB;         // rows past N read as zeros
-        dma_rows<D, RB, false>(make_rsrc(Qh + (size_t)q0 * D, bytes), sQ, wave * (C::BM / 4), C::BM / 4, lane);
-        dma_rows<D, RB, false>(make_rsrc(dOh + (size_t)q0 * D, bytes), sG, wave * (C::BM / 4), C::BM / 4, lane);
+        dma_rows<D, RB, false>(make_rsrc(Qh + (size_t)q0 * D, bytes), sQ, wave * (C::BM / 8), C::BM / 8, lane);
+        dma_rows<D, RB, false>(make_rsrc(dOh + (size_t)q0 * D, bytes), sG, wave * (C::BM / 8), C::BM / 8, lane);
         if (wave == 0)
             lreg = -kLog2e * buf_ld4f(make_rsrc(LSE + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
         if (wave == 1) lreg = buf_ld4f(make_rsrc(Dg + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
@@ -518,56 +522,45 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
 
     auto block_body = [&](int i, const char* sQ, const char* sG, const float* sL, const float* sD) {
         const int q0 = i * C::BM;
-        f32x16 sacc[C::NQT], pacc[C::NQT];
+        f32x16 sacc, pacc;
 #pragma unroll
-        for (int qt = 0; qt < C::NQT; ++qt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { sacc[qt][r] = 0.f; pacc[qt][r] = 0.f; }
+        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
 #pragma unroll
         for (int s = 0; s < C::NKS; ++s) {
-            const bf16x8 kf = tl.row(sK + 32 * wave * RB, 0, s);
-#pragma unroll
-            for (int qt = 0; qt < C::NQT; ++qt) {
-                sacc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sQ, 32 * qt, s), kf, sacc[qt], 0, 0, 0);
-                pacc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sG, 32 * qt, s), vf[s], pacc[qt], 0, 0, 0);
-            }
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sQ, 32 * qh, s), tl.row(sK, 32 * kg, s), sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sG, 32 * qh, s), tl.row(sV, 32 * kg, s), pacc, 0, 0, 0);
         }
-        // (a wave whose keys all follow the block's queries gets P = 0 from the mask;
-        // skipping it instead would split the accumulators' live ranges)
-        const bool need_mask = CAUSAL && (q0 < k0w + 31);
-        bf16x8 pb[C::NQT][2], sb[C::NQT][2];
+        // (a wave whose keys all follow its queries gets P = 0 from the mask; skipping
+        // it instead would split the accumulators' live ranges)
+        const bool need_mask = CAUSAL && (q0 + 32 * qh < k0w + 31);
+        bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int qt = 0; qt < C::NQT; ++qt) {
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int qo = 32 * qh + 8 * g4 + 4 * h;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + qo);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + qo);
+            float p[4];
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int qo = 32 * qt + 8 * g4 + 4 * h;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + qo);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + qo);
-                float p[4];
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(sacc[4 * g4 + e], c2, l4[e]));
+            if (need_mask) {              // key > query -> 0
 #pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(sacc[qt][4 * g4 + e], c2, l4[e]));
-                if (need_mask) {              // key > query -> 0
+                for (int e = 0; e < 4; ++e)
+                    if (mykey > q0 + qo + e) p[e] = 0.f;
+            }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (mykey > q0 + qo + e) p[e] = 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pb[qt][g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e]);
-                    sb[qt][g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e] * (pacc[qt][4 * g4 + e] - d4[e]));
-                }
+            for (int e = 0; e < 4; ++e) {
+                pb[g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e]);
+                sb[g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e] * (pacc[4 * g4 + e] - d4[e]));
             }
         }
 #pragma unroll
-        for (int qt = 0; qt < C::NQT; ++qt)
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt) {
-                    const int k0q = 32 * qt + 16 * s2;
-                    dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sG, k0q, dt), pb[qt][s2], dvacc[dt], 0, 0, 0);
-                    dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sQ, k0q, dt), sb[qt][s2], dkacc[dt], 0, 0, 0);
-                }
+            for (int dt = 0; dt < C::NDT; ++dt) {
+                const int k0q = 32 * qh + 16 * s2;
+                dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sG, k0q, dt), pb[s2], dvacc[dt], 0, 0, 0);
+                dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sQ, k0q, dt), sb[s2], dkacc[dt], 0, 0, 0);
+            }
     };
 
     auto step = [&](int i, char* qc, char* gc, float* lc, float* dc, char* qn, char* gn) {
@@ -587,8 +580,45 @@ __global__ __launch_bounds__(256) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     }
     if (i < nq) step(i, sQ0, sG0, sL0, sD0, sQ1, sG1);
 
-    // dK = scale * dK^T acc, dV = dV^T acc, written once
-    if (mykey < N) {
+    // sum the two query halves' partials: waves 4..7 park theirs in LDS (dK in the
+    // Q/dO buffers, dV in the K/V tiles; lane-contiguous float4s), waves 0..3 add
+    wait_vmem_all();
+    __syncthreads();                                    // every tile fully read
+    {
+        char* dkbuf = kg == 0 ? sQ0 : kg == 1 ? sQ1 : kg == 2 ? sG0 : sG1;
+        char* dvbuf = (kg < 2 ? sK : sV) + (kg & 1) * (C::NDT * 16 * 64 * 4);
+        if (qh == 1) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int o = ((dt * 4 + g4) * 64 + lane) * 16;
+                    *reinterpret_cast<f32x4*>(dkbuf + o) =
+                        f32x4{dkacc[dt][4 * g4], dkacc[dt][4 * g4 + 1], dkacc[dt][4 * g4 + 2], dkacc[dt][4 * g4 + 3]};
+                    *reinterpret_cast<f32x4*>(dvbuf + o) =
+                        f32x4{dvacc[dt][4 * g4], dvacc[dt][4 * g4 + 1], dvacc[dt][4 * g4 + 2], dvacc[dt][4 * g4 + 3]};
+                }
+        }
+        __syncthreads();
+        if (qh == 0) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int o = ((dt * 4 + g4) * 64 + lane) * 16;
+                    const f32x4 pk = *reinterpret_cast<const f32x4*>(dkbuf + o);
+                    const f32x4 pv = *reinterpret_cast<const f32x4*>(dvbuf + o);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        dkacc[dt][4 * g4 + e] += pk[e];
+                        dvacc[dt][4 * g4 + e] += pv[e];
+                    }
+                }
+        }
+    }
+
+    // dK = scale * dK^T acc, dV = dV^T acc, written once (waves 0..3)
+    if (qh == 0 && mykey < N) {
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -822,7 +852,7 @@ static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void
                          const float* Dd, int BH, int N, float scale, void* dK, void* dV, hipStream_t st)
 {
     const int nkblk = (N + BwdKVCfg<D>::BN - 1) / BwdKVCfg<D>::BN;
-    hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G>), dim3(nkblk * BH), dim3(256), 0, st, (const bf16*)Q,
+    hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G>), dim3(nkblk * BH), dim3(64 * BwdKVCfg<D>::WAVES), 0, st, (const bf16*)Q,
                        (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale);
     return hipGetLastError();
 }
