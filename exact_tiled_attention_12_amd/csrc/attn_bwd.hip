@@ -480,9 +480,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     const int kg = wave & 3, qh = wave >> 2;            // key group, query half
     const int l32 = lane & 31, h = lane >> 5;
 
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = bid / nkblk;
-    const int kb = bid - head * nkblk;
+    int head, kb;
+    block_coords<CAUSAL, false>(blockIdx.x, gridDim.x, nkblk, head, kb);
     const int k0 = kb * C::BN;
     const int k0w = k0 + 32 * kg;
     const int mykey = k0w + l32;
@@ -682,10 +681,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
 
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = bid / nqblk;
-    int qb = bid - head * nqblk;
-    if (CAUSAL) qb = nqblk - 1 - qb;                 // heavy row blocks first
+    int head, qb;
+    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + 32 * wave;
     const int myq = q0w + l32;

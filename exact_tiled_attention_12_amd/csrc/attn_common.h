@@ -245,6 +245,11 @@ __device__ __forceinline__ void wait_vmem_leave(int n)
     }
 }
 
+// Instruction classes for __builtin_amdgcn_sched_group_barrier: each call asks the
+// scheduler for a group of n instructions of one class, groups issued in call order.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
 // max(a, b, c) in one v_max3_f32.
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
@@ -278,6 +283,34 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 __device__ __forceinline__ int xcd_remap(int bid, int nb) {
     if ((nb & 7) != 0) return bid;
     return (bid & 7) * (nb >> 3) + (bid >> 3);
+}
+
+// Workgroup -> (head, block).  Non-causal: the blocks of one head run back to back
+// on one XCD (xcd_remap).  Causal: a block's cost grows linearly with its index, so
+// each XCD takes the blocks of its own heads longest-first, the heaviest block of
+// every head before any lighter one, which keeps the tail of the launch short.
+// HEAVY_LAST: a head's last block costs most (query-side kernels); otherwise its
+// first (key-side kernels).
+template <bool CAUSAL, bool HEAVY_LAST>
+__device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int& head, int& blk)
+{
+    if constexpr (!CAUSAL) {
+        const int b = xcd_remap(bid, nb);
+        head = b / nblk;
+        blk = b - head * nblk;
+    } else {
+        const int BH = nb / nblk;
+        int rank;
+        if ((BH & 7) == 0) {
+            const int hx = BH >> 3, k = bid >> 3;
+            rank = k / hx;
+            head = (bid & 7) * hx + (k - rank * hx);
+        } else {
+            rank = bid / BH;
+            head = bid - rank * BH;
+        }
+        blk = HEAVY_LAST ? nblk - 1 - rank : rank;
+    }
 }
 
 }  // namespace attn

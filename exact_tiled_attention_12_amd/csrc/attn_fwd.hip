@@ -408,10 +408,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, h = lane >> 5;
 
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = bid / nqblk;
-    int qb = bid - head * nqblk;
-    if (CAUSAL) qb = nqblk - 1 - qb;                 // heavy row blocks first
+    int head, qb;
+    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + 32 * wave;
     const int myq = q0w + l32;
