@@ -481,7 +481,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, kb;
-    block_coords<CAUSAL, false>(blockIdx.x, gridDim.x, nkblk, head, kb);
+    block_coords<CAUSAL, false, 32>(blockIdx.x, gridDim.x, nkblk, head, kb);
     const int k0 = kb * C::BN;
     const int k0w = k0 + 32 * kg;
     const int mykey = k0w + l32;
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, qb;
-    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, head, qb);
+    block_coords<CAUSAL, true, 64>(blockIdx.x, gridDim.x, nqblk, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + 32 * wave;
     const int myq = q0w + l32;

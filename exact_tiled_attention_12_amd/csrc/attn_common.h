@@ -286,12 +286,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 }
 
 // Workgroup -> (head, block).  Non-causal: the blocks of one head run back to back
-// on one XCD (xcd_remap).  Causal: a block's cost grows linearly with its index, so
-// each XCD takes the blocks of its own heads longest-first, the heaviest block of
-// every head before any lighter one, which keeps the tail of the launch short.
+// on one XCD (xcd_remap).  Causal: a block's cost grows linearly with its index.
+// Each XCD works through its own heads in groups of G, a group's blocks
+// longest-first (the heaviest block of every head in the group before any lighter
+// one), the next group's heavy blocks filling the slots its light blocks free.
+// G is the smallest head count whose blocks fill the XCD's SLOTS workgroup slots,
+// so the tail stays short while the K/V of only G heads compete for the XCD's L2.
 // HEAVY_LAST: a head's last block costs most (query-side kernels); otherwise its
-// first (key-side kernels).
-template <bool CAUSAL, bool HEAVY_LAST>
+// first (key-side kernels).  Without 8 | BH the whole GPU is one group sequence.
+template <bool CAUSAL, bool HEAVY_LAST, int SLOTS>
 __device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int& head, int& blk)
 {
     if constexpr (!CAUSAL) {
@@ -300,15 +303,17 @@ __device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int& hea
         blk = b - head * nblk;
     } else {
         const int BH = nb / nblk;
-        int rank;
-        if ((BH & 7) == 0) {
-            const int hx = BH >> 3, k = bid >> 3;
-            rank = k / hx;
-            head = (bid & 7) * hx + (k - rank * hx);
-        } else {
-            rank = bid / BH;
-            head = bid - rank * BH;
-        }
+        const bool split = (BH & 7) == 0;
+        const int hx = split ? BH >> 3 : BH;            // heads of this XCD (of the GPU)
+        const int k = split ? bid >> 3 : bid;           // position in its sequence
+        const int x = split ? (bid & 7) : 0;
+        const int slots = split ? SLOTS : 8 * SLOTS;
+        const int G = min(hx, (slots + nblk - 1) / nblk);
+        const int g = k / (G * nblk);
+        const int gh = min(G, hx - g * G);              // heads in this group
+        const int kk = k - g * G * nblk;
+        const int rank = kk / gh;
+        head = x * hx + g * G + (kk - rank * gh);
         blk = HEAVY_LAST ? nblk - 1 - rank : rank;
     }
 }

@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, qb;
-    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, head, qb);
+    block_coords<CAUSAL, true, 64>(blockIdx.x, gridDim.x, nqblk, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + 32 * wave;
     const int myq = q0w + l32;
