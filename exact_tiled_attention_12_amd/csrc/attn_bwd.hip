@@ -521,13 +521,32 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
 
     auto block_body = [&](int i, const char* sQ, const char* sG, const float* sL, const float* sD) {
         const int q0 = i * C::BM;
+        // S and dP; their fragments (Q, K, dO, V rows in turn) are read PF ahead through a
+        // small ring (sched_barrier keeps the order)
         f32x16 sacc, pacc;
+        {
+            constexpr int PF = 4, NF = 4 * C::NKS;
+            bf16x8 ring[PF];
+            auto frag = [&](int f) __attribute__((always_inline)) {
+                const int s = f >> 2, w = f & 3;
+                return tl.row(w == 0 ? sQ : w == 1 ? sK : w == 2 ? sG : sV, (w & 1) ? 32 * kg : 32 * qh, s);
+            };
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+            for (int f = 0; f < PF; ++f) ring[f] = frag(f);
 #pragma unroll
-        for (int s = 0; s < C::NKS; ++s) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sQ, 32 * qh, s), tl.row(sK, 32 * kg, s), sacc, 0, 0, 0);
-            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sG, 32 * qh, s), tl.row(sV, 32 * kg, s), pacc, 0, 0, 0);
+            for (int f = 0; f < NF; f += 2) {
+                const bf16x8 a = ring[f % PF], b = ring[(f + 1) % PF];
+                if (f + PF < NF) {
+                    ring[f % PF] = frag(f + PF);
+                    ring[(f + 1) % PF] = frag(f + PF + 1);
+                }
+                const int s = f >> 2;
+                if (f & 2)
+                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s == 0 ? f32x16{} : pacc, 0, 0, 0);
+                else
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s == 0 ? f32x16{} : sacc, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // (a wave whose keys all follow its queries gets P = 0 from the mask; skipping
         // it instead would split the accumulators' live ranges)

@@ -456,11 +456,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+        // K fragments are read PF products ahead through a small ring (sched_barrier keeps the order)
+        {
+            constexpr int NM = C::NKS * C::NKT, PF = 4;
+            bf16x8 ring[PF];
 #pragma unroll
-        for (int s = 0; s < C::NKS; ++s)
+            for (int i = 0; i < PF; ++i) ring[i] = tl.row(sK, 32 * (i % C::NKT), i / C::NKT);
 #pragma unroll
-            for (int kt = 0; kt < C::NKT; ++kt)
-                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sK, 32 * kt, s), qf[s], sacc[kt], 0, 0, 0);
+            for (int i = 0; i < NM; ++i) {
+                const int s = i / C::NKT, kt = i % C::NKT;
+                const bf16x8 a = ring[i % PF];
+                if (i + PF < NM) ring[i % PF] = tl.row(sK, 32 * ((i + PF) % C::NKT), (i + PF) / C::NKT);
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
 
         // lane: query myq, keys kv0 + 32 kt + 8 (r/4) + 4 h + r%4
         const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > q0w) || (kv0 + C::BN > N);
