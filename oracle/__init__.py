@@ -22,9 +22,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        # ATTN_ORACLE_LIB: another build of attn_oracle.c (the mutation test of the pins
+        # loads deliberately broken copies this way, in subprocesses of its own)
+        path = os.environ.get("ATTN_ORACLE_LIB", LIB_PATH)
+        if path == LIB_PATH and not os.path.exists(LIB_PATH):
             _build()
-        lib = ctypes.CDLL(LIB_PATH)
+        lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         lp = ctypes.POINTER(ctypes.c_long)
         L, D, I = ctypes.c_long, ctypes.c_double, ctypes.c_int
