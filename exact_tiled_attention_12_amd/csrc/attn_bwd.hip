@@ -11,22 +11,21 @@
 // point that the backward parallelises over the sequence with little
 // synchronisation between blocks (results answer, section 3 (2)).
 //
-// gfx950 mapping (workgroup = 4 waves; each wave owns 32 keys, BN = 128 keys):
-//   * S = Q K^T and dP = dO V^T with K and V fragments resident in registers:
-//     every accumulator lane holds ONE key and 16 queries, which is exactly the
-//     operand layout the two products that contract over queries need:
-//       dV^T += dO^T P   and   dK^T += Q^T dS   (accumulated in registers).
-//     Q^T and dO^T are staged transposed in LDS for those A operands.
-//   * P = exp2(S * scale * log2e - LSE * log2e): no max, no sum; LSE rows past N
-//     are +inf so their probabilities are exactly 0.
-//   * dQ needs dS with queries on lanes: each wave writes its dS columns to LDS
-//     once, then the workgroup computes dQ = dS K for its 128 keys (K^T kept in
-//     LDS for the whole pass) and adds it into an fp32 accumulator with
-//     hardware float atomics in L2 (coalesced: 32 lanes cover 32 consecutive
-//     head-dim columns of one row).
-//   * Causal: query blocks entirely above the workgroup's keys are never
-//     visited; a wave whose keys all lie after a block's last query skips its
-//     products and contributes zeros to dS.
+// gfx950 mapping.  Every kernel puts ONE key (key-side products) or ONE query
+// (query-side products) on each accumulator lane, which is exactly the operand
+// layout the following product needs:
+//   * key side: S = Q K^T and dP = dO V^T with keys on lanes feed dV^T += dO^T P
+//     and dK^T += Q^T dS, accumulated over all query blocks and written once;
+//   * query side: S^T and dP^T with queries on lanes feed dQ^T += K^T dS^T;
+//   * P = exp2(S * scale * log2e - LSE * log2e): no max and no sum are needed.
+// bf16 inputs (the hot path): a key-side kernel (dK, dV) and a separate
+// query-side kernel (dQ), both written once, no atomics, deterministic; K/V and
+// Q/dO tiles go straight to swizzled LDS (direct-to-LDS loads) and transposed
+// operands come from ds_read_b64_tr_b16.  fp32 inputs: one fused kernel with
+// K and V fragments resident in registers, Q^T/dO^T staged transposed in LDS,
+// and dQ added into a zero-filled fp32 accumulator with float atomics.
+// Causal: query blocks entirely before a workgroup's keys are never visited;
+// waves whose keys all follow a block's queries get P = 0 (or skip the block).
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -79,19 +78,20 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, lo
 // ----------------------------------------------------------------------------
 template <typename T, int D>
 struct BwdCfg {
+    static_assert(sizeof(T) == 4, "the fused kernel serves fp32 inputs");
     static constexpr int THREADS = 256;
     static constexpr int BN = 128;                       // keys per workgroup (32 per wave)
-    static constexpr int BM = sizeof(T) == 2 ? 64 : 32;  // query rows per iteration
+    static constexpr int BM = 32;                        // query rows per iteration
     static constexpr int NQT = BM / 32;
     static constexpr int DP = (D + 31) / 32 * 32;
     static constexpr int NDT = DP / 32;
     static constexpr int E = Mma<T>::E, KS = Mma<T>::KS, CH = Mma<T>::CH;
     static constexpr int NKS = D / KS;                   // steps over the head dim
     static constexpr int CPR = D / CH;
-    static constexpr int QPITCH = D + (sizeof(T) == 2 ? 8 : 4);   // Qs, dOs  [BM][QPITCH]
+    static constexpr int QPITCH = D + 4;                          // Qs, dOs  [BM][QPITCH]
     static constexpr int TPITCH = BM + 4;                         // Qt, dOt  [DP][TPITCH]
-    static constexpr int SPITCH = BN + (sizeof(T) == 2 ? 8 : 4);  // dS       [BM][SPITCH]
-    static constexpr int KTPITCH = BN + (sizeof(T) == 2 ? 8 : 4); // Kt       [DP][KTPITCH]
+    static constexpr int SPITCH = BN + 4;                         // dS       [BM][SPITCH]
+    static constexpr int KTPITCH = BN + 4;                        // Kt       [DP][KTPITCH]
     static constexpr int OFF_QS = 0;
     static constexpr int OFF_DOS = OFF_QS + BM * QPITCH;
     static constexpr int OFF_QT = OFF_DOS + BM * QPITCH;
@@ -108,36 +108,24 @@ struct BwdCfg {
     static_assert(D % KS == 0 && D % CH == 0, "head dim");
 };
 
-// Transposed store of a 4-row x 1-chunk group: for each of the chunk's CH
+// Transposed store of a 4-row x 1-chunk group (fp32): for each of the chunk's 4
 // columns, the 4 rows' values are written contiguously at dst[col][row0..row0+3].
-template <typename T>
-__device__ __forceinline__ void store_transposed4(T* base, int pitch, int col0, int row0, const u32x4 (&v)[4])
+__device__ __forceinline__ void store_transposed4(float* base, int pitch, int col0, int row0, const u32x4 (&v)[4])
 {
-    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t lo0 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x05040100u);
-            const uint32_t lo1 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x05040100u);
-            const uint32_t hi0 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x07060302u);
-            const uint32_t hi1 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x07060302u);
-            *reinterpret_cast<u32x2*>(base + (col0 + 2 * w) * pitch + row0) = u32x2{lo0, lo1};
-            *reinterpret_cast<u32x2*>(base + (col0 + 2 * w + 1) * pitch + row0) = u32x2{hi0, hi1};
-        }
-    } else {
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-            st16(base + (col0 + x) * pitch + row0, u32x4{v[0][x], v[1][x], v[2][x], v[3][x]});
-    }
+    for (int x = 0; x < 4; ++x)
+        st16(base + (col0 + x) * pitch + row0, u32x4{v[0][x], v[1][x], v[2][x], v[3][x]});
 }
 
-template <typename T, int D, bool CAUSAL, typename G>
-__global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                  const T* __restrict__ V, const T* __restrict__ dO,
-                                                  const float* __restrict__ LSE,
-                                                  const float* __restrict__ Dg,
-                                                  float* __restrict__ dQacc, G* __restrict__ dK,
-                                                  G* __restrict__ dV, int N, int nkblk, float scale)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_kernel_f32(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ V, const float* __restrict__ dO,
+                                                      const float* __restrict__ LSE,
+                                                      const float* __restrict__ Dg,
+                                                      float* __restrict__ dQacc, float* __restrict__ dK,
+                                                      float* __restrict__ dV, int N, int nkblk, float scale)
 {
+    typedef float T;
     using C = BwdCfg<T, D>;
     using M = Mma<T>;
     typedef typename M::frag frag;
@@ -156,9 +144,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
 
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = bid / nkblk;
-    const int kb = bid - head * nkblk;
+    int head, kb;
+    block_coords<CAUSAL, false, 32>(blockIdx.x, gridDim.x, nkblk, head, kb);
     const int k0 = kb * C::BN;
     const int k0w = k0 + 32 * wave;            // this wave's first key
     const int mykey = k0w + l32;
@@ -177,15 +164,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
     frag kf[C::NKS], vf[C::NKS];
 #pragma unroll
     for (int s = 0; s < C::NKS; ++s) {
-        if constexpr (sizeof(T) == 2) {
-            const bool ok = mykey < N;
-            kf[s] = __builtin_bit_cast(bf16x8, ok ? ld16(Kh + (size_t)mykey * D + s * C::KS + C::E * h) : zero4());
-            vf[s] = __builtin_bit_cast(bf16x8, ok ? ld16(Vh + (size_t)mykey * D + s * C::KS + C::E * h) : zero4());
-        } else {
-            const bool ok = mykey < N;
-            kf[s] = ok ? Kh[(size_t)mykey * D + s * C::KS + h] : 0.f;
-            vf[s] = ok ? Vh[(size_t)mykey * D + s * C::KS + h] : 0.f;
-        }
+        const bool ok = mykey < N;
+        kf[s] = ok ? Kh[(size_t)mykey * D + s * C::KS + h] : 0.f;
+        vf[s] = ok ? Vh[(size_t)mykey * D + s * C::KS + h] : 0.f;
     }
 
     // ---- K^T of the workgroup's keys in LDS (B operand of dQ = dS K); pad rows zeroed ----
@@ -197,7 +178,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
             const int key = k0 + 4 * g + e;
             v[e] = key < N ? ld16(Kh + (size_t)key * D + col * C::CH) : zero4();
         }
-        store_transposed4<T>(Kt, C::KTPITCH, col * C::CH, 4 * g, v);
+        store_transposed4(Kt, C::KTPITCH, col * C::CH, 4 * g, v);
     }
     if constexpr (C::DP > D) {
         for (int x = tid; x < (C::DP - D) * C::KTPITCH; x += C::THREADS) Kt[D * C::KTPITCH + x] = from_f32<T>(0.f);
@@ -252,8 +233,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
                     st16(Qs + (4 * g + e) * C::QPITCH + col * C::CH, qst[it][e]);
                     st16(dOs + (4 * g + e) * C::QPITCH + col * C::CH, gst[it][e]);
                 }
-                store_transposed4<T>(Qt, C::TPITCH, col * C::CH, 4 * g, qst[it]);
-                store_transposed4<T>(dOt, C::TPITCH, col * C::CH, 4 * g, gst[it]);
+                store_transposed4(Qt, C::TPITCH, col * C::CH, 4 * g, qst[it]);
+                store_transposed4(dOt, C::TPITCH, col * C::CH, 4 * g, gst[it]);
             }
         }
         if (tid < C::BM) { lse_l[tid] = lst; d_l[tid] = dst_; }
@@ -288,14 +269,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
 #pragma unroll
                 for (int qt = 0; qt < C::NQT; ++qt) {
                     const int off = (32 * qt + l32) * C::QPITCH + s * C::KS + C::E * h;
-                    frag a, g;
-                    if constexpr (sizeof(T) == 2) {
-                        a = __builtin_bit_cast(bf16x8, ld16(Qs + off));
-                        g = __builtin_bit_cast(bf16x8, ld16(dOs + off));
-                    } else {
-                        a = Qs[off];
-                        g = dOs[off];
-                    }
+                    const frag a = Qs[off], g = dOs[off];
                     sacc[qt] = M::mma(a, kf[s], sacc[qt]);
                     pacc[qt] = M::mma(g, vf[s], pacc[qt]);
                 }
@@ -326,37 +300,12 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
             for (int qt = 0; qt < C::NQT; ++qt) {
 #pragma unroll
                 for (int s2 = 0; s2 < 32 / C::KS; ++s2) {
-                    frag bp, bs;
-                    if constexpr (sizeof(T) == 2) {
-                        bf16x8 x, y;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            x[e] = to_bf16(sacc[qt][8 * s2 + e]);
-                            y[e] = to_bf16(pacc[qt][8 * s2 + e]);
-                        }
-                        bp = x;
-                        bs = y;
-                    } else {
-                        bp = sacc[qt][s2];
-                        bs = pacc[qt][s2];
-                    }
+                    const frag bp = sacc[qt][s2], bs = pacc[qt][s2];
 #pragma unroll
                     for (int dt = 0; dt < C::NDT; ++dt) {
                         const int rowoff = (32 * dt + l32) * C::TPITCH + 32 * qt;
-                        frag ag, aq;
-                        if constexpr (sizeof(T) == 2) {
-                            const int o0 = rowoff + 16 * s2 + 4 * h, o1 = o0 + 8;
-                            const u32x2 g0 = *reinterpret_cast<const u32x2*>(dOt + o0);
-                            const u32x2 g1 = *reinterpret_cast<const u32x2*>(dOt + o1);
-                            const u32x2 q0v = *reinterpret_cast<const u32x2*>(Qt + o0);
-                            const u32x2 q1v = *reinterpret_cast<const u32x2*>(Qt + o1);
-                            ag = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
-                            aq = __builtin_bit_cast(bf16x8, u32x4{q0v[0], q0v[1], q1v[0], q1v[1]});
-                        } else {
-                            const int o = rowoff + 8 * (s2 >> 2) + 4 * h + (s2 & 3);
-                            ag = dOt[o];
-                            aq = Qt[o];
-                        }
+                        const int o = rowoff + 8 * (s2 >> 2) + 4 * h + (s2 & 3);
+                        const frag ag = dOt[o], aq = Qt[o];
                         dvacc[dt] = M::mma(ag, bp, dvacc[dt]);
                         dkacc[dt] = M::mma(aq, bs, dkacc[dt]);
                     }
@@ -382,15 +331,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
             for (int s = 0; s < C::BN / C::KS; ++s) {
                 const T* pa = dSl + (32 * qt + l32) * C::SPITCH + s * C::KS + C::E * h;
                 const T* pb = Kt + (32 * dt + l32) * C::KTPITCH + s * C::KS + C::E * h;
-                frag a, b;
-                if constexpr (sizeof(T) == 2) {
-                    a = __builtin_bit_cast(bf16x8, ld16(pa));
-                    b = __builtin_bit_cast(bf16x8, ld16(pb));
-                } else {
-                    a = *pa;
-                    b = *pb;
-                }
-                acc = M::mma(a, b, acc);
+                acc = M::mma(*pa, *pb, acc);
             }
             const int dcol = 32 * dt + l32;
             if (dcol < D) {
@@ -411,21 +352,11 @@ __global__ __launch_bounds__(256) void bwd_kernel(const T* __restrict__ Q, const
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d0 = 32 * dt + 8 * g4 + 4 * h;
                 if (d0 < D) {
-                    G* pk = dK + hoff + (size_t)mykey * D + d0;
-                    G* pv = dV + hoff + (size_t)mykey * D + d0;
-                    if constexpr (sizeof(G) == 4) {
-                        f32x4 a, b;
+                    f32x4 a, b;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) { a[e] = dkacc[dt][4 * g4 + e] * scale; b[e] = dvacc[dt][4 * g4 + e]; }
-                        *reinterpret_cast<f32x4*>(pk) = a;
-                        *reinterpret_cast<f32x4*>(pv) = b;
-                    } else {
-                        bf16x4 a, b;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) { a[e] = to_bf16(dkacc[dt][4 * g4 + e] * scale); b[e] = to_bf16(dvacc[dt][4 * g4 + e]); }
-                        *reinterpret_cast<bf16x4*>(pk) = a;
-                        *reinterpret_cast<bf16x4*>(pv) = b;
-                    }
+                    for (int e = 0; e < 4; ++e) { a[e] = dkacc[dt][4 * g4 + e] * scale; b[e] = dvacc[dt][4 * g4 + e]; }
+                    *reinterpret_cast<f32x4*>(dK + hoff + (size_t)mykey * D + d0) = a;
+                    *reinterpret_cast<f32x4*>(dV + hoff + (size_t)mykey * D + d0) = b;
                 }
             }
     }
@@ -920,7 +851,7 @@ static hipError_t f32_t(const void* Q, const void* K, const void* V, const void*
     const long n4 = (long)BH * N * D / 4;
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dQacc, n4);
     const int nkblk = (N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL((bwd_kernel<float, D, CAUSAL, float>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
+    hipLaunchKernelGGL((bwd_kernel_f32<D, CAUSAL>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
                        (const float*)Q, (const float*)K, (const float*)V, (const float*)dO, LSE, Dd, dQacc, dK,
                        dV, N, nkblk, scale);
     return hipGetLastError();

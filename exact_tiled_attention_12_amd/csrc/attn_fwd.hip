@@ -1,6 +1,6 @@
-// Forward kernel: O = softmax(scale Q K^T) V and LSE, one fused pass.
+// Forward kernels: O = softmax(scale Q K^T) V and LSE, one fused pass.
 //
-// What it follows: FlashAttention-2 review, 'core algorithm' answer, section 2
+// What they follow: FlashAttention-2 review, 'core algorithm' answer, section 2
 // (1) tiling into T_r row blocks and T_c column blocks, (2) per-block S, P and
 // P V with the running max m and running sum l, (3) one final adjustment;
 // "IO-4 FlashAttention", sections 3-4 (block algorithm, online softmax).
@@ -8,32 +8,33 @@
 // exchanges partial results with other waves): FlashAttention-2 review, the
 // Split-K vs Split-Q answer, section 2.
 //
-// gfx950 mapping (one workgroup = 4 waves = 256 threads per block of BM query
-// rows; each wave owns 32*QT rows):
-//   * The wave computes S^T = K Q^T with bf16 MFMA 32x32x16 (fp32 MFMA
-//     32x32x2 for fp32 inputs), so every lane of the accumulator holds ONE
-//     query and 16 keys.  The running max, running sum and rescale factor are
-//     then per-lane scalars; the only cross-lane step per tile is one exchange
-//     with lane l^32, which holds the other 16 keys of the same query.
-//   * O^T = V^T P^T: the S^T accumulator registers, rounded to bf16, ARE the
-//     B operand of the next MFMA (the contraction over keys is permuted to the
-//     accumulator's row order, and V^T is read with the same permutation).
-//   * K tiles are staged row-major in LDS, V tiles transposed (key fastest)
-//     so that each lane reads its 4+4 keys with two 8-byte LDS reads.  Both
-//     are double-buffered; the next tile's global loads are in flight while
-//     the current tile is multiplied (one barrier per tile).
+// gfx950 mapping shared by both kernels (one workgroup = 4 waves = 256 threads
+// per block of 128 query rows; each wave owns 32 rows):
+//   * The wave computes S^T = K Q^T with MFMA 32x32 tiles, so every lane of the
+//     accumulator holds ONE query and 16 keys.  The running max, running sum and
+//     rescale factor are then per-lane scalars; the only cross-lane step per
+//     tile is one exchange with lane l^32, which holds the other 16 keys of the
+//     same query.
+//   * O^T = V^T P^T: the S^T accumulator registers (rounded to the MFMA operand
+//     type) ARE the B operand of the next MFMA (the contraction over keys is
+//     permuted to the accumulator's row order, and V^T is read with the same
+//     permutation).
 //   * Causal: column tiles entirely above the block's diagonal are never
 //     loaded; tiles entirely above a wave's own rows are skipped by that wave;
 //     the element mask runs only on tiles that cross the diagonal or N.
-//   * Blocks of one head run on one XCD (shared L2 for its K, V); with a
-//     causal mask the heaviest row blocks of a head start first.
+//
+// fwd_kernel_f32 (fp32 inputs, MFMA 32x32x2 f32) stages K and V through
+// registers into padded LDS (V transposed, key fastest); fwd_kernel_bf16 below
+// is the bf16 hot path.
 #include "attn_common.h"
 #include "attn_launch.h"
 
 namespace attn {
 
-template <typename T, int D, int QT>
+template <typename T, int D>
 struct FwdCfg {
+    static_assert(sizeof(T) == 4, "the staged kernel serves fp32 inputs");
+    static constexpr int QT = 1;
     static constexpr int THREADS = 256;
     static constexpr int BM = 4 * 32 * QT;          // query rows per workgroup
     static constexpr int BN = 64;                   // keys per tile
@@ -42,7 +43,7 @@ struct FwdCfg {
     static constexpr int NDT = DP / 32;
     static constexpr int E = Mma<T>::E, KS = Mma<T>::KS, CH = Mma<T>::CH;
     static constexpr int NKS = D / KS;              // MFMA steps of the Q K^T contraction
-    static constexpr int KPITCH = D + (sizeof(T) == 2 ? 8 : 4);   // elements; conflict-free b128 reads
+    static constexpr int KPITCH = D + 4;                          // elements; conflict-free b128 reads
     static constexpr int VPITCH = BN + 4;                         // elements
     static constexpr int KBUF = BN * KPITCH;
     static constexpr int VBUF = DP * VPITCH;
@@ -57,27 +58,26 @@ struct FwdCfg {
     static_assert(SMEM_ELEMS * sizeof(T) <= 160 * 1024, "LDS budget");
 };
 
-template <typename T, int D, bool CAUSAL, int QT, int MINW>
-__global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                        const T* __restrict__ V, T* __restrict__ O,
-                                                        float* __restrict__ LSE, int N, int nqblk, float c,
-                                                        int negate_q)
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_kernel_f32(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ V, float* __restrict__ O,
+                                                      float* __restrict__ LSE, int N, int nqblk, float c,
+                                                      int negate_q)
 {
-    using C = FwdCfg<T, D, QT>;
+    typedef float T;
+    using C = FwdCfg<T, D>;
+    constexpr int QT = C::QT;
     using M = Mma<T>;
     typedef typename M::frag frag;
     constexpr float NEG_INF = -__builtin_inff();
-    constexpr bool BF = sizeof(T) == 2;
 
     __shared__ __attribute__((aligned(16))) T smem[C::SMEM_ELEMS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
 
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int head = bid / nqblk;
-    int qb = bid - head * nqblk;
-    if (CAUSAL) qb = nqblk - 1 - qb;                 // heavy row blocks first
+    int head, qb;
+    block_coords<CAUSAL, true, 32>(blockIdx.x, gridDim.x, nqblk, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + wave * 32 * QT;             // this wave's first query row
     const size_t hoff = (size_t)head * (size_t)N * D;
@@ -95,14 +95,8 @@ __global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
             for (int s = 0; s < C::NKS; ++s) {
                 const uint32_t off = rowoff + (s * C::KS + C::E * h) * sizeof(T);
-                if constexpr (BF) {
-                    u32x4 raw = buf_ld16(rq, off);
-                    if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-                    qf[t][s] = __builtin_bit_cast(bf16x8, raw);
-                } else {
-                    const float x = buf_ld4f(rq, off);
-                    qf[t][s] = negate_q ? -x : x;
-                }
+                const float x = buf_ld4f(rq, off);
+                qf[t][s] = negate_q ? -x : x;
             }
         }
     }
@@ -174,25 +168,11 @@ __global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q,
         for (int i = 0; i < C::VLD; ++i)
             if (C::VGROUPS % C::THREADS == 0 || tid + C::THREADS * i < C::VGROUPS) {
                 const int g = vst_g[i], col = vst_col[i];
-                if constexpr (BF) {
-                    // 4 keys x 8 head-dim values -> for each of the 8 dims, 4 keys (8 bytes).
+                // 4 keys x 4 head-dim values -> for each of the 4 dims, the 4 keys (16 bytes)
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const uint32_t lo0 = __builtin_amdgcn_perm(vst[i][1][w], vst[i][0][w], 0x05040100u);
-                        const uint32_t lo1 = __builtin_amdgcn_perm(vst[i][3][w], vst[i][2][w], 0x05040100u);
-                        const uint32_t hi0 = __builtin_amdgcn_perm(vst[i][1][w], vst[i][0][w], 0x07060302u);
-                        const uint32_t hi1 = __builtin_amdgcn_perm(vst[i][3][w], vst[i][2][w], 0x07060302u);
-                        const int dd = col * C::CH + 2 * w;
-                        *reinterpret_cast<u32x2*>(Vl + dd * C::VPITCH + 4 * g) = u32x2{lo0, lo1};
-                        *reinterpret_cast<u32x2*>(Vl + (dd + 1) * C::VPITCH + 4 * g) = u32x2{hi0, hi1};
-                    }
-                } else {
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int dd = col * C::CH + x;
-                        st16(Vl + dd * C::VPITCH + 4 * g,
-                             u32x4{vst[i][0][x], vst[i][1][x], vst[i][2][x], vst[i][3][x]});
-                    }
+                for (int x = 0; x < 4; ++x) {
+                    const int dd = col * C::CH + x;
+                    st16(Vl + dd * C::VPITCH + 4 * g, u32x4{vst[i][0][x], vst[i][1][x], vst[i][2][x], vst[i][3][x]});
                 }
             }
     };
@@ -212,9 +192,7 @@ __global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
             for (int kt = 0; kt < C::NKT; ++kt) {
                 const T* src = Kl + (32 * kt + l32) * C::KPITCH + s * C::KS + C::E * h;
-                frag a;
-                if constexpr (BF) a = __builtin_bit_cast(bf16x8, ld16(src));
-                else a = *src;
+                const frag a = *src;
 #pragma unroll
                 for (int t = 0; t < QT; ++t) sacc[kt][t] = M::mma(a, qf[t][s], sacc[kt][t]);
             }
@@ -272,24 +250,7 @@ __global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q,
                     for (int r = 0; r < 16; ++r) sacc[kt][t][r] = fast_exp2(fmaf(sacc[kt][t][r], c, -ms));
             }
             // P in the MFMA operand type; the row sum is taken over exactly these values.
-            if constexpr (BF) {
-                float ls[2] = {0.f, 0.f};
-#pragma unroll
-                for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        bf16x8 pb;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) pb[e] = to_bf16(sacc[kt][t][8 * s2 + e]);
-                        const u32x4 w = __builtin_bit_cast(u32x4, pb);
-                        ls[s2] = sum2_bf16(w[0], ls[s2]);
-                        ls[s2] = sum2_bf16(w[1], ls[s2]);
-                        ls[s2] = sum2_bf16(w[2], ls[s2]);
-                        ls[s2] = sum2_bf16(w[3], ls[s2]);
-                        pf[kt][s2][t] = pb;
-                    }
-                l[t] += ls[0] + ls[1];
-            } else {
+            {
                 float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kt = 0; kt < C::NKT; ++kt)
@@ -310,14 +271,7 @@ __global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q,
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt) {
                     const T* vrow = Vl + (32 * dt + l32) * C::VPITCH + 32 * kt;
-                    frag a;
-                    if constexpr (BF) {
-                        const u32x2 x0 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 4 * h);
-                        const u32x2 x1 = *reinterpret_cast<const u32x2*>(vrow + 16 * s2 + 8 + 4 * h);
-                        a = __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
-                    } else {
-                        a = vrow[8 * (s2 >> 2) + 4 * h + (s2 & 3)];
-                    }
+                    const frag a = vrow[8 * (s2 >> 2) + 4 * h + (s2 & 3)];
 #pragma unroll
                     for (int t = 0; t < QT; ++t) oacc[dt][t] = M::mma(a, pf[kt][s2][t], oacc[dt][t]);
                 }
@@ -354,18 +308,10 @@ __global__ __launch_bounds__(256, MINW) void fwd_kernel(const T* __restrict__ Q,
                 for (int g = 0; g < 4; ++g) {
                     const int d0 = 32 * dt + 8 * g + 4 * h;
                     if (d0 < D) {
-                        T* dst = Oh + (size_t)q * D + d0;
-                        if constexpr (BF) {
-                            bf16x4 v;
+                        f32x4 v;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] = to_bf16(oacc[dt][t][4 * g + e] * inv);
-                            *reinterpret_cast<bf16x4*>(dst) = v;
-                        } else {
-                            f32x4 v;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] = oacc[dt][t][4 * g + e] * inv;
-                            *reinterpret_cast<f32x4*>(dst) = v;
-                        }
+                        for (int e = 0; e < 4; ++e) v[e] = oacc[dt][t][4 * g + e] * inv;
+                        *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + d0) = v;
                     }
                 }
             if (h == 0) LSE[(size_t)head * N + q] = (mc[t] + __log2f(lt)) * kLn2;
@@ -578,16 +524,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
     }
 }
 
-template <typename T, int D, bool CAUSAL, int QT, int MINW>
-static hipError_t launch_fwd_t(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               int BH, int N, float scale, hipStream_t st)
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
+                                 float scale, hipStream_t st)
 {
-    using C = FwdCfg<T, D, QT>;
+    using C = FwdCfg<float, D>;
     const int nqblk = (N + C::BM - 1) / C::BM;
     const float c = fabsf(scale) * kLog2e;
     const int negq = scale < 0.f;
-    hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, QT, MINW>), dim3(nqblk * BH), dim3(C::THREADS), 0, st,
-                       (const T*)Q, (const T*)K, (const T*)V, (T*)O, LSE, N, nqblk, c, negq);
+    hipLaunchKernelGGL((fwd_kernel_f32<D, CAUSAL>), dim3(nqblk * BH), dim3(C::THREADS), 0, st, (const float*)Q,
+                       (const float*)K, (const float*)V, (float*)O, LSE, N, nqblk, c, negq);
     return hipGetLastError();
 }
 
@@ -610,8 +556,8 @@ static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void
         if (causal) return launch_fwd_bf16<D, true>(Q, K, V, O, LSE, BH, N, scale, st);
         return launch_fwd_bf16<D, false>(Q, K, V, O, LSE, BH, N, scale, st);
     } else {
-        if (causal) return launch_fwd_t<T, D, true, 1, 1>(Q, K, V, O, LSE, BH, N, scale, st);
-        return launch_fwd_t<T, D, false, 1, 1>(Q, K, V, O, LSE, BH, N, scale, st);
+        if (causal) return launch_fwd_f32<D, true>(Q, K, V, O, LSE, BH, N, scale, st);
+        return launch_fwd_f32<D, false>(Q, K, V, O, LSE, BH, N, scale, st);
     }
 }
 
