@@ -1,8 +1,9 @@
 """Exact tiled attention (fused forward + recomputing backward) for MI355X / gfx950.
 
 The compute lives in libattn.so (HIP kernels behind the C ABI in
-include/attn.h); this package holds its ctypes binding, the build step, the
+include/attn.h); this package holds its ctypes binding, the autograd wrapper, the build step, the
 workload shapes, the seeded input generator and the FLOP accounting.
 """
 from .attn import (attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_main, attn_bwd_preprocess,  # noqa: F401
                    attn_bwd_workspace_bytes, attn_fwd, lib, AttnError, LIB_PATH)
+from .autograd import FlashAttentionFn, flash_attention  # noqa: F401
