@@ -19,7 +19,9 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
-            "attn_bwd_workspace_bytes", "attn_bwd", "attn_status_str", "attn_last_hip_error")
+            "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
+            "attn_status_str", "attn_last_hip_error")
+MASK_BLOCK = 128        # ATTN_MASK_BLOCK: rows and keys per block-mask entry
 
 _lib = None
 
@@ -49,8 +51,11 @@ def lib():
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = sz
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, i, vp, sz, vp]
+        L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, vp]
+        L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, vp, i, vp,
+                                           sz, vp]
         for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
-                     "attn_bwd"):
+                     "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse"):
             getattr(L, name).restype = i
         L.attn_status_str.argtypes = [i]
         L.attn_status_str.restype = ctypes.c_char_p
@@ -183,5 +188,59 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, grad_dtype=torch.flo
     dq, dk, dv = mk(dq), mk(dk), mk(dv)
     _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), gdt, _ptr(workspace),
+          ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q, stream))
+    return dq, dk, dv
+
+
+def _block_mask(mask, q):
+    """(uint8 device mask, mask_heads) from a [T, T] mask or a [B, H, T, T] one (nonzero = kept)."""
+    B, H, N, _ = _shape(q)
+    T = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    if mask.dtype != torch.uint8:
+        raise TypeError("block mask must be uint8")
+    if tuple(mask.shape) == (T, T):
+        heads = 1
+    elif tuple(mask.shape) == (B, H, T, T):
+        heads = B * H
+    else:
+        raise ValueError(f"block mask must be [{T}, {T}] or [{B}, {H}, {T}, {T}]")
+    _check_inputs(q, mask)
+    return mask, heads
+
+
+def attn_fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None, lse=None, stream=None):
+    """Forward restricted to the kept blocks of block_mask (uint8 [T, T] or [B, H, T, T],
+    T = ceil(N / 128)).  Rows that keep no key get O = 0 and LSE = -inf.  Returns (O, LSE)."""
+    B, H, N, d = _shape(q)
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    _check_inputs(q, k, v)
+    m, heads = _block_mask(block_mask, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_inputs(q, o, l)
+    _call("attn_fwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, float(scale),
+          int(bool(causal)), _ptr(m), heads, _ptr(o), _ptr(l), _stream(q, stream))
+    return o, l
+
+
+def attn_bwd_blocksparse(q, k, v, o, do, lse, block_mask, scale=None, causal=False, grad_dtype=torch.float32,
+                         workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """Backward of attn_fwd_blocksparse (same mask, scale and causal flag).  Returns (dQ, dK, dV)."""
+    B, H, N, d = _shape(q)
+    _check_inputs(q, k, v, o, do, lse)
+    m, heads = _block_mask(block_mask, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    gdt = ATTN_BF16 if grad_dtype == torch.bfloat16 else ATTN_F32
+    need = attn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    mk = lambda t: torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) if t is None else t
+    dq, dk, dv = mk(dq), mk(dk), mk(dv)
+    _call("attn_bwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
+          float(scale), int(bool(causal)), _ptr(m), heads, _ptr(dq), _ptr(dk), _ptr(dv), gdt, _ptr(workspace),
           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q, stream))
     return dq, dk, dv

@@ -60,7 +60,7 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, attn_dtype dt,
     if (s != ATTN_OK) return s;
     if (!dtype_ok(dt) || !isfinite(scale) || (causal != 0 && causal != 1)) return ATTN_EINVAL;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return ATTN_EINVAL;
-    return from_hip(attn::launch_fwd(Q, K, V, O, LSE, dt == ATTN_BF16, B * H, N, d, scale, causal,
+    return from_hip(attn::launch_fwd(Q, K, V, O, LSE, dt == ATTN_BF16, B * H, N, d, scale, causal, nullptr, 0,
                                      (hipStream_t)stream));
 }
 
@@ -93,8 +93,8 @@ attn_status attn_bwd_dkdv(const void* Q, const void* K, const void* V, const voi
     if (s != ATTN_OK) return s;
     if (!aligned16(dK) || !aligned16(dV)) return ATTN_EINVAL;
     if (dt != ATTN_BF16) return ATTN_EUNSUPPORTED;
-    return from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dK, dV, false,
-                                          (hipStream_t)stream));
+    return from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dK, dV, false, nullptr,
+                                          0, (hipStream_t)stream));
 }
 
 attn_status attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
@@ -105,7 +105,7 @@ attn_status attn_bwd_dq(const void* Q, const void* K, const void* V, const void*
     if (s != ATTN_OK) return s;
     if (!aligned16(dQ)) return ATTN_EINVAL;
     if (dt != ATTN_BF16) return ATTN_EUNSUPPORTED;
-    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false,
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false, nullptr, 0,
                                         (hipStream_t)stream));
 }
 
@@ -118,10 +118,12 @@ attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const voi
     if (!aligned16(dQ) || !aligned16(dK) || !aligned16(dV)) return ATTN_EINVAL;
     hipStream_t st = (hipStream_t)stream;
     if (dt == ATTN_F32)
-        return from_hip(attn::launch_bwd_f32(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, dK, dV, st));
-    attn_status r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dK, dV, false, st));
+        return from_hip(attn::launch_bwd_f32(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, dK, dV, nullptr, 0,
+                                             st));
+    attn_status r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dK, dV, false,
+                                                   nullptr, 0, st));
     if (r != ATTN_OK) return r;
-    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false, st));
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false, nullptr, 0, st));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d)
@@ -130,10 +132,10 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d)
     return round256((size_t)B * H * N * sizeof(float));
 }
 
-attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                     const float* LSE, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
-                     void* dQ, void* dK, void* dV, attn_dtype grad_dt, void* workspace,
-                     size_t workspace_bytes, void* stream)
+static attn_status bwd_all(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                           const float* LSE, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                           const unsigned char* bmask, long mhead, void* dQ, void* dK, void* dV,
+                           attn_dtype grad_dt, void* workspace, size_t workspace_bytes, void* stream)
 {
     attn_status s = check_bwd_args(Q, K, V, dO, LSE, (const float*)workspace, dt, B, H, N, d, scale, causal);
     if (s != ATTN_OK) return s;
@@ -150,10 +152,56 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
     if (r != ATTN_OK) return r;
     if (!bf_in)
         return from_hip(attn::launch_bwd_f32(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, (float*)dQ, (float*)dK,
-                                             (float*)dV, st));
-    r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dK, dV, bf_grad, st));
+                                             (float*)dV, bmask, mhead, st));
+    r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dK, dV, bf_grad, bmask, mhead,
+                                       st));
     if (r != ATTN_OK) return r;
-    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dQ, bf_grad, st));
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dQ, bf_grad, bmask, mhead,
+                                        st));
+}
+
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* LSE, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                     void* dQ, void* dK, void* dV, attn_dtype grad_dt, void* workspace,
+                     size_t workspace_bytes, void* stream)
+{
+    return bwd_all(Q, K, V, O, dO, LSE, dt, B, H, N, d, scale, causal, nullptr, 0, dQ, dK, dV, grad_dt, workspace,
+                   workspace_bytes, stream);
+}
+
+// bytes between the masks of consecutive heads, or -1 for a bad mask argument
+static long mask_head_stride(const unsigned char* block_mask, int mask_heads, int B, int H, int N)
+{
+    if (block_mask == nullptr) return -1;
+    if (mask_heads != 1 && (long long)mask_heads != (long long)B * H) return -1;
+    const long T = (N + ATTN_MASK_BLOCK - 1) / ATTN_MASK_BLOCK;
+    return mask_heads == 1 ? 0 : T * T;
+}
+
+attn_status attn_fwd_blocksparse(const void* Q, const void* K, const void* V, attn_dtype dt, int B, int H, int N,
+                                 int d, float scale, int causal, const unsigned char* block_mask, int mask_heads,
+                                 void* O, float* LSE, void* stream)
+{
+    attn_status s = check_shape(B, H, N, d);
+    if (s != ATTN_OK) return s;
+    if (!dtype_ok(dt) || !isfinite(scale) || (causal != 0 && causal != 1)) return ATTN_EINVAL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return ATTN_EINVAL;
+    const long mhead = mask_head_stride(block_mask, mask_heads, B, H, N);
+    if (mhead < 0) return ATTN_EINVAL;
+    return from_hip(attn::launch_fwd(Q, K, V, O, LSE, dt == ATTN_BF16, B * H, N, d, scale, causal, block_mask,
+                                     mhead, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                 const float* LSE, attn_dtype dt, int B, int H, int N, int d, float scale,
+                                 int causal, const unsigned char* block_mask, int mask_heads, void* dQ, void* dK,
+                                 void* dV, attn_dtype grad_dt, void* workspace, size_t workspace_bytes,
+                                 void* stream)
+{
+    const long mhead = mask_head_stride(block_mask, mask_heads, B, H, N);
+    if (mhead < 0) return ATTN_EINVAL;
+    return bwd_all(Q, K, V, O, dO, LSE, dt, B, H, N, d, scale, causal, block_mask, mhead, dQ, dK, dV, grad_dt,
+                   workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -117,16 +117,18 @@ __device__ __forceinline__ void store_transposed4(float* base, int pitch, int co
         st16(base + (col0 + x) * pitch + row0, u32x4{v[0][x], v[1][x], v[2][x], v[3][x]});
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) void bwd_kernel_f32(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, const float* __restrict__ dO,
                                                       const float* __restrict__ LSE,
                                                       const float* __restrict__ Dg,
                                                       float* __restrict__ dQacc, float* __restrict__ dK,
-                                                      float* __restrict__ dV, int N, int nkblk, float scale)
+                                                      float* __restrict__ dV, int N, int nkblk, float scale,
+                                                      const uint8_t* __restrict__ bmask, long mhead)
 {
     typedef float T;
     using C = BwdCfg<T, D>;
+    static_assert(kMaskBlock == C::BN && kMaskBlock % C::BM == 0, "mask block = key block");
     using M = Mma<T>;
     typedef typename M::frag frag;
 
@@ -240,13 +242,27 @@ __global__ __launch_bounds__(256) void bwd_kernel_f32(const float* __restrict__ 
         if (tid < C::BM) { lse_l[tid] = lst; d_l[tid] = dst_; }
     };
 
-    if (i0 < nq) load_q(i0);
-    for (int i = i0; i < nq; ++i) {
+    // the query blocks to visit: all from i0 on, or (block-sparse) those of kept mask rows
+    // (kMaskBlock / BM query blocks per mask block); this workgroup's keys are mask column kb
+    MaskWalk mw;
+    constexpr int U = kMaskBlock / C::BM;
+    if constexpr (SPARSE) {
+        const int nmb = (N + kMaskBlock - 1) / kMaskBlock;
+        mw.init(bmask + head * mhead + kb, nmb, nmb, lane);
+    }
+    auto next_block = [&](int i) __attribute__((always_inline)) {
+        if constexpr (SPARSE) return mw.next_unit(i, nq, U, lane);
+        else return i;
+    };
+    int i = next_block(i0);
+    if (i < nq) load_q(i);
+    for (int in; i < nq; i = in) {
+        in = next_block(i + 1);
         const int q0 = i * C::BM;
         __syncthreads();                 // previous iteration's LDS readers are done
         store_q();
         __syncthreads();
-        if (i + 1 < nq) load_q(i + 1);
+        if (in < nq) load_q(in);
 
         const bool skip = CAUSAL && (k0w > q0 + C::BM - 1);   // all of this wave's keys after the block
         if (skip) {
@@ -391,14 +407,15 @@ struct BwdKVCfg {
     static_assert(NDT * 16 * 64 * 4 <= Q_BYTES, "dK partial fits a Q/dO buffer");
 };
 
-template <int D, bool CAUSAL, typename G>
+template <int D, bool CAUSAL, typename G, bool SPARSE>
 __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE, const float* __restrict__ Dg,
                                                      G* __restrict__ dK, G* __restrict__ dV, int N, int nkblk,
-                                                     float scale)
+                                                     float scale, const uint8_t* __restrict__ bmask, long mhead)
 {
     using C = BwdKVCfg<D>;
+    static_assert(kMaskBlock == C::BN && kMaskBlock == 2 * C::BM, "mask block = key block");
     constexpr int RB = C::RB;
     constexpr uint32_t ROWB = D * 2;                    // global bytes per row
     __shared__ __attribute__((aligned(1024))) char sQ0[C::Q_BYTES], sQ1[C::Q_BYTES];
@@ -512,22 +529,49 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
             }
     };
 
-    auto step = [&](int i, char* qc, char* gc, float* lc, float* dc, char* qn, char* gn) {
-        wait_vmem_all();                                // this wave's loads of block i landed
-        if (wave == 0) lc[lane] = lreg;
-        if (wave == 1) dc[lane] = lreg;
-        __syncthreads();                                // everyone's loads landed; block i-1 fully read
-        if (i + 1 < nq) issue_block(i + 1, qn, gn);
-        block_body(i, qc, gc, lc, dc);
-    };
-
-    issue_block(i0, sQ0, sG0);
-    int i = i0;
-    for (; i + 1 < nq; i += 2) {
-        step(i, sQ0, sG0, sL0, sD0, sQ1, sG1);
-        step(i + 1, sQ1, sG1, sL1, sD1, sQ0, sG0);
+    if constexpr (!SPARSE) {
+        auto step = [&](int i, char* qc, char* gc, float* lc, float* dc, char* qn, char* gn) {
+            wait_vmem_all();                            // this wave's loads of block i landed
+            if (wave == 0) lc[lane] = lreg;
+            if (wave == 1) dc[lane] = lreg;
+            __syncthreads();                            // everyone's loads landed; block i-1 fully read
+            if (i + 1 < nq) issue_block(i + 1, qn, gn);
+            block_body(i, qc, gc, lc, dc);
+        };
+        issue_block(i0, sQ0, sG0);
+        int i = i0;
+        for (; i + 1 < nq; i += 2) {
+            step(i, sQ0, sG0, sL0, sD0, sQ1, sG1);
+            step(i + 1, sQ1, sG1, sL1, sD1, sQ0, sG0);
+        }
+        if (i < nq) step(i, sQ0, sG0, sL0, sD0, sQ1, sG1);
+    } else {
+        // in: the next query block to visit (nq if none)
+        auto step = [&](int i, int in, char* qc, char* gc, float* lc, float* dc, char* qn, char* gn) {
+            wait_vmem_all();
+            if (wave == 0) lc[lane] = lreg;
+            if (wave == 1) dc[lane] = lreg;
+            __syncthreads();
+            if (in < nq) issue_block(in, qn, gn);
+            block_body(i, qc, gc, lc, dc);
+        };
+        // only the query blocks of kept mask rows (two 64-query blocks per mask block);
+        // this workgroup's keys are mask column kb
+        const int nmb = (N + kMaskBlock - 1) / kMaskBlock;
+        MaskWalk mw;
+        mw.init(bmask + head * mhead + kb, nmb, nmb, lane);
+        int i = mw.next_unit(i0, nq, 2, lane);
+        if (i < nq) issue_block(i, sQ0, sG0);
+        while (i < nq) {
+            int in = mw.next_unit(i + 1, nq, 2, lane);
+            step(i, in, sQ0, sG0, sL0, sD0, sQ1, sG1);
+            i = in;
+            if (i >= nq) break;
+            in = mw.next_unit(i + 1, nq, 2, lane);
+            step(i, in, sQ1, sG1, sL1, sD1, sQ0, sG0);
+            i = in;
+        }
     }
-    if (i < nq) step(i, sQ0, sG0, sL0, sD0, sQ1, sG1);
 
     // sum the two query halves' partials: waves 4..7 park theirs in LDS (dK in the
     // Q/dO buffers, dV in the K/V tiles; lane-contiguous float4s), waves 0..3 add
@@ -615,13 +659,15 @@ struct BwdQCfg {
     static_assert(4 * T_BYTES <= 80 * 1024, "two workgroups per CU");
 };
 
-template <int D, bool CAUSAL, typename G>
+template <int D, bool CAUSAL, typename G, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                       const bf16* __restrict__ V, const bf16* __restrict__ dO,
                                                       const float* __restrict__ LSE, const float* __restrict__ Dg,
-                                                      G* __restrict__ dQ, int N, int nqblk, float scale)
+                                                      G* __restrict__ dQ, int N, int nqblk, float scale,
+                                                      const uint8_t* __restrict__ bmask, long mhead)
 {
     using C = BwdQCfg<D>;
+    static_assert(kMaskBlock == C::BM && kMaskBlock == 2 * C::BN, "mask block = query block");
     constexpr int RB = C::RB;
     constexpr uint32_t ROWB = D * 2;
     __shared__ __attribute__((aligned(1024))) char sK0[C::T_BYTES], sK1[C::T_BYTES];
@@ -710,21 +756,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
                                                                         dqacc[dt], 0, 0, 0);
     };
 
-    auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
-        wait_vmem_all();
-        __syncthreads();
-        if (j + 1 < ntiles) issue_tile(j + 1, kn, vn);
-        if (!(CAUSAL && j * C::BN > q0w + 31))          // else every key of the tile follows this wave's rows
-            tile_body(j, kc, vc);
-    };
-
-    issue_tile(0, sK0, sV0);
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        step(j, sK0, sV0, sK1, sV1);
-        step(j + 1, sK1, sV1, sK0, sV0);
+    if constexpr (!SPARSE) {
+        auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
+            wait_vmem_all();
+            __syncthreads();
+            if (j + 1 < ntiles) issue_tile(j + 1, kn, vn);
+            if (!(CAUSAL && j * C::BN > q0w + 31))      // else every key of the tile follows this wave's rows
+                tile_body(j, kc, vc);
+        };
+        issue_tile(0, sK0, sV0);
+        int j = 0;
+        for (; j + 1 < ntiles; j += 2) {
+            step(j, sK0, sV0, sK1, sV1);
+            step(j + 1, sK1, sV1, sK0, sV0);
+        }
+        if (j < ntiles) step(j, sK0, sV0, sK1, sV1);
+    } else {
+        // jn: the next tile to visit (ntiles if none)
+        auto step = [&](int j, int jn, const char* kc, const char* vc, char* kn, char* vn) {
+            wait_vmem_all();
+            __syncthreads();
+            if (jn < ntiles) issue_tile(jn, kn, vn);
+            if (!(CAUSAL && j * C::BN > q0w + 31)) tile_body(j, kc, vc);
+        };
+        // only the tiles of kept key blocks (two 64-key tiles per mask block)
+        const int nmb = (N + kMaskBlock - 1) / kMaskBlock;
+        MaskWalk mw;
+        mw.init(bmask + head * mhead + (size_t)qb * nmb, 1, nmb, lane);
+        int j = mw.next_unit(0, ntiles, 2, lane);
+        if (j < ntiles) issue_tile(j, sK0, sV0);
+        while (j < ntiles) {
+            int jn = mw.next_unit(j + 1, ntiles, 2, lane);
+            step(j, jn, sK0, sV0, sK1, sV1);
+            j = jn;
+            if (j >= ntiles) break;
+            jn = mw.next_unit(j + 1, ntiles, 2, lane);
+            step(j, jn, sK1, sV1, sK0, sV0);
+            j = jn;
+        }
     }
-    if (j < ntiles) step(j, sK0, sV0, sK1, sV1);
 
     // dQ = scale * dQ^T acc (lane = query; 4 consecutive head-dim values per store)
     if (myq < N) {
@@ -796,21 +866,34 @@ hipError_t launch_bwd_pre(const void* O, const void* dO, bool bf16_in, int BH, i
 
 template <int D, bool CAUSAL, typename G>
 static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                         const float* Dd, int BH, int N, float scale, void* dK, void* dV, hipStream_t st)
+                         const float* Dd, int BH, int N, float scale, void* dK, void* dV, const uint8_t* bmask,
+                         long mhead, hipStream_t st)
 {
     const int nkblk = (N + BwdKVCfg<D>::BN - 1) / BwdKVCfg<D>::BN;
-    hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G>), dim3(nkblk * BH), dim3(64 * BwdKVCfg<D>::WAVES), 0, st, (const bf16*)Q,
-                       (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale);
+    const dim3 grid(nkblk * BH), block(64 * BwdKVCfg<D>::WAVES);
+    if (bmask)
+        hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G, true>), grid, block, 0, st, (const bf16*)Q, (const bf16*)K,
+                           (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, bmask, mhead);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G, false>), grid, block, 0, st, (const bf16*)Q, (const bf16*)K,
+                           (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, nullptr, 0L);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, typename G>
 static hipError_t dq_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                       const float* Dd, int BH, int N, float scale, void* dQ, hipStream_t st)
+                       const float* Dd, int BH, int N, float scale, void* dQ, const uint8_t* bmask, long mhead,
+                       hipStream_t st)
 {
     const int nqblk = (N + BwdQCfg<D>::BM - 1) / BwdQCfg<D>::BM;
-    hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
-                       (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale);
+    if (bmask)
+        hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G, true>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
+                           (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale, bmask,
+                           mhead);
+    else
+        hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G, false>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
+                           (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale,
+                           nullptr, 0L);
     return hipGetLastError();
 }
 
@@ -830,45 +913,49 @@ static hipError_t dq_t(const void* Q, const void* K, const void* V, const void* 
 
 hipError_t launch_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                            const float* Dd, int BH, int N, int d, float scale, int causal, void* dK, void* dV,
-                           bool bf16_grad, hipStream_t st)
+                           bool bf16_grad, const uint8_t* bmask, long mhead, hipStream_t st)
 {
-    ATTN_DISPATCH_D_CAUSAL_G(dkdv_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dK, dV, st)
+    ATTN_DISPATCH_D_CAUSAL_G(dkdv_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dK, dV, bmask, mhead, st)
 }
 
 hipError_t launch_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                          const float* Dd, int BH, int N, int d, float scale, int causal, void* dQ, bool bf16_grad,
-                         hipStream_t st)
+                         const uint8_t* bmask, long mhead, hipStream_t st)
 {
-    ATTN_DISPATCH_D_CAUSAL_G(dq_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dQ, st)
+    ATTN_DISPATCH_D_CAUSAL_G(dq_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dQ, bmask, mhead, st)
 }
 
 template <int D, bool CAUSAL>
 static hipError_t f32_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                         const float* Dd, int BH, int N, float scale, float* dQacc, float* dK, float* dV,
-                        hipStream_t st)
+                        const uint8_t* bmask, long mhead, hipStream_t st)
 {
     using C = BwdCfg<float, D>;
     const long n4 = (long)BH * N * D / 4;
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dQacc, n4);
     const int nkblk = (N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL((bwd_kernel_f32<D, CAUSAL>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
-                       (const float*)Q, (const float*)K, (const float*)V, (const float*)dO, LSE, Dd, dQacc, dK,
-                       dV, N, nkblk, scale);
+    if (bmask)
+        hipLaunchKernelGGL((bwd_kernel_f32<D, CAUSAL, true>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
+                           (const float*)Q, (const float*)K, (const float*)V, (const float*)dO, LSE, Dd, dQacc, dK,
+                           dV, N, nkblk, scale, bmask, mhead);
+    else
+        hipLaunchKernelGGL((bwd_kernel_f32<D, CAUSAL, false>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
+                           (const float*)Q, (const float*)K, (const float*)V, (const float*)dO, LSE, Dd, dQacc, dK,
+                           dV, N, nkblk, scale, nullptr, 0L);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_f32(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                           const float* Dd, int BH, int N, int d, float scale, int causal, float* dQacc, float* dK,
-                          float* dV, hipStream_t st)
+                          float* dV, const uint8_t* bmask, long mhead, hipStream_t st)
 {
+#define ATTN_F32_ARGS Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, bmask, mhead, st
     switch (d) {
-        case 64: return causal ? f32_t<64, true>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st)
-                               : f32_t<64, false>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
-        case 80: return causal ? f32_t<80, true>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st)
-                               : f32_t<80, false>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
-        case 128: return causal ? f32_t<128, true>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st)
-                                : f32_t<128, false>(Q, K, V, dO, LSE, Dd, BH, N, scale, dQacc, dK, dV, st);
+        case 64: return causal ? f32_t<64, true>(ATTN_F32_ARGS) : f32_t<64, false>(ATTN_F32_ARGS);
+        case 80: return causal ? f32_t<80, true>(ATTN_F32_ARGS) : f32_t<80, false>(ATTN_F32_ARGS);
+        case 128: return causal ? f32_t<128, true>(ATTN_F32_ARGS) : f32_t<128, false>(ATTN_F32_ARGS);
     }
+#undef ATTN_F32_ARGS
     return hipErrorInvalidValue;
 }
 

@@ -318,4 +318,60 @@ __device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int& hea
     }
 }
 
+// ---------------------------------------------------------------------------
+// Block-sparse masks.  A mask is uint8 [T][T] per head, T = ceil(N / kMaskBlock):
+// entry (a, b) nonzero keeps the scores of query block a against key block b,
+// zero drops them, so the kernels never load those tiles (FlashAttention-2
+// review, 'sparse/hybrid' answer, section 3 (1): block-level sparse operation,
+// only the important blocks are processed on chip).  kMaskBlock is a multiple
+// of every kernel's tile edge (64 or 128 rows/keys, 32-row steps).
+// ---------------------------------------------------------------------------
+constexpr int kMaskBlock = 128;
+
+// Walks the kept entries of one mask row (stride 1) or column (stride T) in
+// increasing order.  The entries of a 64-block window sit in a wave-uniform bit
+// mask (one byte load per lane and one ballot per window), so stepping to the
+// next kept block is scalar work.  Every call must be made by all lanes of the
+// wave, in wave-uniform control flow.
+struct MaskWalk {
+    const uint8_t* p;
+    int stride, nb, w0;
+    uint64_t win;
+
+    __device__ __forceinline__ void load(int base, int lane)
+    {
+        w0 = base;
+        const int b = base + lane;
+        const bool kept = b < nb && p[(size_t)b * stride] != 0;
+        win = __builtin_amdgcn_ballot_w64(kept);
+    }
+    __device__ __forceinline__ void init(const uint8_t* entries, int stride_, int nblocks, int lane)
+    {
+        p = entries;
+        stride = stride_;
+        nb = nblocks;
+        load(0, lane);
+    }
+    // smallest kept block >= b (nb if none); b never decreases between calls
+    __device__ __forceinline__ int next(int b, int lane)
+    {
+#pragma nounroll
+        while (b < nb) {
+            if (b >= w0 + 64) load(b, lane);
+            const uint64_t bits = win >> (b - w0);
+            if (bits != 0) return b + (int)__builtin_ctzll(bits);
+            b = w0 + 64;
+        }
+        return nb;
+    }
+    // smallest unit >= u (U units per mask block) whose block is kept, or u_end
+    __device__ __forceinline__ int next_unit(int u, int u_end, int U, int lane)
+    {
+        if (u >= u_end) return u_end;
+        const int b = next(u / U, lane);
+        const int v = b == u / U ? u : b * U;
+        return v < u_end ? v : u_end;
+    }
+};
+
 }  // namespace attn

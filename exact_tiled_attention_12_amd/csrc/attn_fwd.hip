@@ -26,8 +26,11 @@
 // fwd_kernel_f32 (fp32 inputs, MFMA 32x32x2 f32) stages K and V through
 // registers into padded LDS (V transposed, key fastest); fwd_kernel_bf16 below
 // is the bf16 hot path.
+#include "../../include/attn.h"
 #include "attn_common.h"
 #include "attn_launch.h"
+
+static_assert(ATTN_MASK_BLOCK == attn::kMaskBlock, "the ABI's mask block is the kernels'");
 
 namespace attn {
 
@@ -58,14 +61,15 @@ struct FwdCfg {
     static_assert(SMEM_ELEMS * sizeof(T) <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) void fwd_kernel_f32(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int N, int nqblk, float c,
-                                                      int negate_q)
+                                                      int negate_q, const uint8_t* __restrict__ bmask, long mhead)
 {
     typedef float T;
     using C = FwdCfg<T, D>;
+    static_assert(kMaskBlock == 2 * C::BN && kMaskBlock == C::BM, "mask block = query block");
     constexpr int QT = C::QT;
     using M = Mma<T>;
     typedef typename M::frag frag;
@@ -280,18 +284,44 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(const float* __restrict__ 
     };
 
     // ---- main loop, unrolled by two so the LDS buffer offsets are constants ----
-    auto step = [&](int j, T* Kl) {
-        store_tile(Kl);
-        __syncthreads();
-        if (j + 1 < ntiles) load_tile(j + 1);
-        const int kv0 = j * C::BN;
-        if (!(CAUSAL && kv0 > q0w + 32 * QT - 1))        // else: every key is above this wave's rows
-            compute_tile(Kl, kv0);
-    };
-    load_tile(0);
-    for (int j = 0; j < ntiles; j += 2) {
-        step(j, smem);
-        if (j + 1 < ntiles) step(j + 1, smem + C::KBUF + C::VBUF);
+    if constexpr (!SPARSE) {
+        auto step = [&](int j, T* Kl) {
+            store_tile(Kl);
+            __syncthreads();
+            if (j + 1 < ntiles) load_tile(j + 1);
+            const int kv0 = j * C::BN;
+            if (!(CAUSAL && kv0 > q0w + 32 * QT - 1))    // else: every key is above this wave's rows
+                compute_tile(Kl, kv0);
+        };
+        load_tile(0);
+        for (int j = 0; j < ntiles; j += 2) {
+            step(j, smem);
+            if (j + 1 < ntiles) step(j + 1, smem + C::KBUF + C::VBUF);
+        }
+    } else {
+        // jn: the next tile to visit (ntiles if none)
+        auto step = [&](int j, int jn, T* Kl) {
+            store_tile(Kl);
+            __syncthreads();
+            if (jn < ntiles) load_tile(jn);
+            const int kv0 = j * C::BN;
+            if (!(CAUSAL && kv0 > q0w + 32 * QT - 1)) compute_tile(Kl, kv0);
+        };
+        // only the tiles of kept key blocks (two 64-key tiles per mask block)
+        const int nmb = (N + kMaskBlock - 1) / kMaskBlock;
+        MaskWalk mw;
+        mw.init(bmask + head * mhead + (size_t)qb * nmb, 1, nmb, lane);
+        int j = mw.next_unit(0, ntiles, 2, lane);
+        if (j < ntiles) load_tile(j);
+        while (j < ntiles) {
+            int jn = mw.next_unit(j + 1, ntiles, 2, lane);
+            step(j, jn, smem);
+            j = jn;
+            if (j >= ntiles) break;
+            jn = mw.next_unit(j + 1, ntiles, 2, lane);
+            step(j, jn, smem + C::KBUF + C::VBUF);
+            j = jn;
+        }
     }
 
     // ---- epilogue: one division by l, O and LSE written once ----
@@ -299,7 +329,7 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(const float* __restrict__ 
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
         const float lt = l[t] + xor32(l[t]);
-        const float inv = 1.0f / lt;
+        const float inv = (SPARSE && !(lt > 0.f)) ? 0.f : 1.0f / lt;     // no kept key: O = 0, LSE = -inf
         const int q = q0w + 32 * t + l32;
         if (q < N) {
 #pragma unroll
@@ -337,12 +367,14 @@ struct FwdBf16Cfg {
     static_assert(4 * T_BYTES <= 80 * 1024, "two workgroups per CU");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                           const bf16* __restrict__ V, bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int N, int nqblk, float c,
-                                                          int negate_q)
+                                                          int negate_q, const uint8_t* __restrict__ bmask,
+                                                          long mhead)
 {
+    static_assert(kMaskBlock == 2 * FwdBf16Cfg<D>::BN && kMaskBlock == FwdBf16Cfg<D>::BM, "mask block = query block");
     using C = FwdBf16Cfg<D>;
     constexpr int RB = C::RB;
     constexpr uint32_t ROWB = D * 2;
@@ -487,25 +519,50 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
                                                                        oacc[dt], 0, 0, 0);
     };
 
-    auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
-        wait_vmem_all();                                // this wave's loads of tile j landed
-        __syncthreads();                                // everyone's; tile j-1 fully read
-        if (j + 1 < ntiles) issue_tile(j + 1, kn, vn);
-        if (!(CAUSAL && j * C::BN > q0w + 31))          // else every key follows this wave's rows
-            tile_body(j, kc, vc);
-    };
-
-    issue_tile(0, sK0, sV0);
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        step(j, sK0, sV0, sK1, sV1);
-        step(j + 1, sK1, sV1, sK0, sV0);
+    if constexpr (!SPARSE) {
+        auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
+            wait_vmem_all();                            // this wave's loads of tile j landed
+            __syncthreads();                            // everyone's; tile j-1 fully read
+            if (j + 1 < ntiles) issue_tile(j + 1, kn, vn);
+            if (!(CAUSAL && j * C::BN > q0w + 31))      // else every key follows this wave's rows
+                tile_body(j, kc, vc);
+        };
+        issue_tile(0, sK0, sV0);
+        int j = 0;
+        for (; j + 1 < ntiles; j += 2) {
+            step(j, sK0, sV0, sK1, sV1);
+            step(j + 1, sK1, sV1, sK0, sV0);
+        }
+        if (j < ntiles) step(j, sK0, sV0, sK1, sV1);
+    } else {
+        // jn: the next tile to visit (ntiles if none)
+        auto step = [&](int j, int jn, const char* kc, const char* vc, char* kn, char* vn) {
+            wait_vmem_all();
+            __syncthreads();
+            if (jn < ntiles) issue_tile(jn, kn, vn);
+            if (!(CAUSAL && j * C::BN > q0w + 31)) tile_body(j, kc, vc);
+        };
+        // only the tiles of kept key blocks (two 64-key tiles per mask block)
+        const int nmb = (N + kMaskBlock - 1) / kMaskBlock;
+        MaskWalk mw;
+        mw.init(bmask + head * mhead + (size_t)qb * nmb, 1, nmb, lane);
+        int j = mw.next_unit(0, ntiles, 2, lane);
+        if (j < ntiles) issue_tile(j, sK0, sV0);
+        while (j < ntiles) {
+            int jn = mw.next_unit(j + 1, ntiles, 2, lane);
+            step(j, jn, sK0, sV0, sK1, sV1);
+            j = jn;
+            if (j >= ntiles) break;
+            jn = mw.next_unit(j + 1, ntiles, 2, lane);
+            step(j, jn, sK1, sV1, sK0, sV0);
+            j = jn;
+        }
     }
-    if (j < ntiles) step(j, sK0, sV0, sK1, sV1);
 
-    // epilogue: one division by l, O and LSE written once
+    // epilogue: one division by l, O and LSE written once (a row with no kept key:
+    // O = 0 and LSE = -inf)
     const float lt = l + xor32(l);
-    const float inv = 1.0f / lt;
+    const float inv = (SPARSE && !(lt > 0.f)) ? 0.f : 1.0f / lt;
     if (myq < N) {
         bf16* dst = O + hoff + (size_t)myq * D;
 #pragma unroll
@@ -524,57 +581,67 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
-                                 float scale, hipStream_t st)
+                                 float scale, const uint8_t* bmask, long mhead, hipStream_t st)
 {
     using C = FwdCfg<float, D>;
     const int nqblk = (N + C::BM - 1) / C::BM;
     const float c = fabsf(scale) * kLog2e;
     const int negq = scale < 0.f;
-    hipLaunchKernelGGL((fwd_kernel_f32<D, CAUSAL>), dim3(nqblk * BH), dim3(C::THREADS), 0, st, (const float*)Q,
-                       (const float*)K, (const float*)V, (float*)O, LSE, N, nqblk, c, negq);
+    hipLaunchKernelGGL((fwd_kernel_f32<D, CAUSAL, SPARSE>), dim3(nqblk * BH), dim3(C::THREADS), 0, st,
+                       (const float*)Q, (const float*)K, (const float*)V, (float*)O, LSE, N, nqblk, c, negq, bmask,
+                       mhead);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
-                                  float scale, hipStream_t st)
+                                  float scale, const uint8_t* bmask, long mhead, hipStream_t st)
 {
     const int nqblk = (N + FwdBf16Cfg<D>::BM - 1) / FwdBf16Cfg<D>::BM;
-    hipLaunchKernelGGL((fwd_kernel_bf16<D, CAUSAL>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
+    hipLaunchKernelGGL((fwd_kernel_bf16<D, CAUSAL, SPARSE>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
                        (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk, fabsf(scale) * kLog2e,
-                       (int)(scale < 0.f));
+                       (int)(scale < 0.f), bmask, mhead);
     return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               int BH, int N, float scale, int causal, hipStream_t st)
+template <bool BF, int D, bool CAUSAL>
+static hipError_t launch_fwd_dc(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
+                                float scale, const uint8_t* bmask, long mhead, hipStream_t st)
 {
-    if constexpr (sizeof(T) == 2) {
-        if (causal) return launch_fwd_bf16<D, true>(Q, K, V, O, LSE, BH, N, scale, st);
-        return launch_fwd_bf16<D, false>(Q, K, V, O, LSE, BH, N, scale, st);
+    if constexpr (BF) {
+        if (bmask) return launch_fwd_bf16<D, CAUSAL, true>(Q, K, V, O, LSE, BH, N, scale, bmask, mhead, st);
+        return launch_fwd_bf16<D, CAUSAL, false>(Q, K, V, O, LSE, BH, N, scale, nullptr, 0, st);
     } else {
-        if (causal) return launch_fwd_f32<D, true>(Q, K, V, O, LSE, BH, N, scale, st);
-        return launch_fwd_f32<D, false>(Q, K, V, O, LSE, BH, N, scale, st);
+        if (bmask) return launch_fwd_f32<D, CAUSAL, true>(Q, K, V, O, LSE, BH, N, scale, bmask, mhead, st);
+        return launch_fwd_f32<D, CAUSAL, false>(Q, K, V, O, LSE, BH, N, scale, nullptr, 0, st);
     }
 }
 
+template <bool BF, int D>
+static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
+                               float scale, int causal, const uint8_t* bmask, long mhead, hipStream_t st)
+{
+    if (causal) return launch_fwd_dc<BF, D, true>(Q, K, V, O, LSE, BH, N, scale, bmask, mhead, st);
+    return launch_fwd_dc<BF, D, false>(Q, K, V, O, LSE, BH, N, scale, bmask, mhead, st);
+}
+
 hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, bool bf16_in,
-                      int BH, int N, int d, float scale, int causal, hipStream_t st)
+                      int BH, int N, int d, float scale, int causal, const uint8_t* bmask, long mhead,
+                      hipStream_t st)
 {
     if (bf16_in) {
         switch (d) {
-            case 64: return launch_fwd_d<bf16, 64>(Q, K, V, O, LSE, BH, N, scale, causal, st);
-            case 80: return launch_fwd_d<bf16, 80>(Q, K, V, O, LSE, BH, N, scale, causal, st);
-            case 128: return launch_fwd_d<bf16, 128>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+            case 64: return launch_fwd_d<true, 64>(Q, K, V, O, LSE, BH, N, scale, causal, bmask, mhead, st);
+            case 80: return launch_fwd_d<true, 80>(Q, K, V, O, LSE, BH, N, scale, causal, bmask, mhead, st);
+            case 128: return launch_fwd_d<true, 128>(Q, K, V, O, LSE, BH, N, scale, causal, bmask, mhead, st);
         }
     } else {
         switch (d) {
-            case 64: return launch_fwd_d<float, 64>(Q, K, V, O, LSE, BH, N, scale, causal, st);
-            case 80: return launch_fwd_d<float, 80>(Q, K, V, O, LSE, BH, N, scale, causal, st);
-            case 128: return launch_fwd_d<float, 128>(Q, K, V, O, LSE, BH, N, scale, causal, st);
+            case 64: return launch_fwd_d<false, 64>(Q, K, V, O, LSE, BH, N, scale, causal, bmask, mhead, st);
+            case 80: return launch_fwd_d<false, 80>(Q, K, V, O, LSE, BH, N, scale, causal, bmask, mhead, st);
+            case 128: return launch_fwd_d<false, 128>(Q, K, V, O, LSE, BH, N, scale, causal, bmask, mhead, st);
         }
     }
     return hipErrorInvalidValue;

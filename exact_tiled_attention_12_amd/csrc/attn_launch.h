@@ -2,11 +2,17 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace attn {
 
+// Every launcher takes an optional block-sparse mask: bmask = uint8 [heads][T][T],
+// T = ceil(N / 128), nonzero = kept (nullptr: dense); mhead = bytes between the
+// masks of consecutive heads (0: one mask for every head).
+
 hipError_t launch_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, bool bf16_in,
-                      int BH, int N, int d, float scale, int causal, hipStream_t st);
+                      int BH, int N, int d, float scale, int causal, const uint8_t* bmask, long mhead,
+                      hipStream_t st);
 
 // D = rowsum(dO o O)
 hipError_t launch_bwd_pre(const void* O, const void* dO, bool bf16_in, int BH, int N, int d, float* D,
@@ -16,15 +22,15 @@ hipError_t launch_bwd_pre(const void* O, const void* dO, bool bf16_in, int BH, i
 // gradients written once in fp32 or bf16.
 hipError_t launch_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                            const float* D, int BH, int N, int d, float scale, int causal, void* dK, void* dV,
-                           bool bf16_grad, hipStream_t st);
+                           bool bf16_grad, const uint8_t* bmask, long mhead, hipStream_t st);
 hipError_t launch_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                          const float* D, int BH, int N, int d, float scale, int causal, void* dQ, bool bf16_grad,
-                         hipStream_t st);
+                         const uint8_t* bmask, long mhead, hipStream_t st);
 
 // fp32 inputs: zero dQacc, then one kernel for all three gradients (dQ by atomics).
 hipError_t launch_bwd_f32(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                           const float* D, int BH, int N, int d, float scale, int causal, float* dQacc, float* dK,
-                          float* dV, hipStream_t st);
+                          float* dV, const uint8_t* bmask, long mhead, hipStream_t st);
 
 hipError_t launch_f32_to_bf16(const float* src, void* dst, long n, hipStream_t st);
 

@@ -34,3 +34,21 @@ def config_inputs(cfg, with_grad=None):
     if with_grad is None:
         with_grad = cfg.backward
     return make_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed, cfg.qk_mult, with_grad)
+
+
+def random_block_mask(T, density, seed, empty_rows=(), lead=()):
+    """uint8 block mask of shape lead + (T, T): each entry kept with probability `density`
+    (seeded), then the listed block rows cleared (queries that keep no key)."""
+    g = torch.Generator().manual_seed(int(seed))
+    m = (torch.rand(tuple(lead) + (T, T), generator=g) < density).to(torch.uint8)
+    for a in empty_rows:
+        m[..., a, :] = 0
+    return m
+
+
+def local_global_mask(T, window, n_global):
+    """uint8 [T, T] block mask of a local + global pattern: query block a keeps key blocks
+    b with |a - b| < window (local context) and the first n_global key blocks (global)."""
+    a = torch.arange(T).view(T, 1)
+    b = torch.arange(T).view(1, T)
+    return (((a - b).abs() < window) | (b < n_global)).to(torch.uint8)

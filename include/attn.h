@@ -114,6 +114,35 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                      void* dQ, void* dK, void* dV, attn_dtype grad_dt,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Block-sparse attention.  FlashAttention-2 review, 'sparse/hybrid' answer,
+ * section 3 (1) (Sparse FlashAttention): the score matrix is cut into blocks,
+ * only the important blocks are computed, and the skipped ones are never moved
+ * on chip.  Here a block mask decides which blocks count:
+ *   block_mask: device uint8 [mask_heads][T][T], T = ceil(N / ATTN_MASK_BLOCK),
+ *     row-major, no alignment needed.  Entry (a, b) nonzero keeps the scores of
+ *     queries a*128 .. a*128+127 against keys b*128 .. b*128+127; zero drops
+ *     them (S = -inf there: P = 0 and the K, V, Q, dO rows of the block are not
+ *     loaded for it).  Applied on top of the causal mask when causal = 1.
+ *   mask_heads: 1 (one mask for every head) or B*H (one per head, [B, H] order);
+ *     anything else, or block_mask = NULL, gives ATTN_EINVAL.
+ * A query row that keeps no key at all gets O = 0 and LSE = -inf, and adds
+ * nothing to any gradient (its own dQ row is 0).  Every other argument, output
+ * and error follows attn_fwd / attn_bwd; the backward must get the forward's
+ * mask, scale and causal flag. */
+#define ATTN_MASK_BLOCK 128
+
+attn_status attn_fwd_blocksparse(const void* Q, const void* K, const void* V, attn_dtype dt,
+                                 int B, int H, int N, int d, float scale, int causal,
+                                 const unsigned char* block_mask, int mask_heads,
+                                 void* O, float* LSE, void* stream);
+
+attn_status attn_bwd_blocksparse(const void* Q, const void* K, const void* V, const void* O,
+                                 const void* dO, const float* LSE, attn_dtype dt,
+                                 int B, int H, int N, int d, float scale, int causal,
+                                 const unsigned char* block_mask, int mask_heads,
+                                 void* dQ, void* dK, void* dV, attn_dtype grad_dt,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_status_str(attn_status s);
 

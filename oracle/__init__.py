@@ -30,12 +30,12 @@ def _load():
         lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         lp = ctypes.POINTER(ctypes.c_long)
-        L, D, I = ctypes.c_long, ctypes.c_double, ctypes.c_int
-        lib.oracle_fwd.argtypes = [dp, dp, dp, L, L, D, I, dp, dp, dp]
-        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, L, L, D, I, dp, dp, dp, dp, dp]
-        lib.oracle_fwd_online.argtypes = [dp, dp, dp, L, L, D, I, L, L, dp, dp]
-        lib.oracle_rows.argtypes = [dp, dp, dp, dp, L, L, D, I, lp, L, dp, dp, dp]
-        lib.oracle_cols.argtypes = [dp, dp, dp, dp, L, L, D, I, lp, L, dp, dp]
+        L, D, I, M = ctypes.c_long, ctypes.c_double, ctypes.c_int, ctypes.c_void_p
+        lib.oracle_fwd.argtypes = [dp, dp, dp, L, L, D, I, M, L, dp, dp, dp]
+        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, L, L, D, I, M, L, dp, dp, dp, dp, dp]
+        lib.oracle_fwd_online.argtypes = [dp, dp, dp, L, L, D, I, M, L, L, L, dp, dp]
+        lib.oracle_rows.argtypes = [dp, dp, dp, dp, L, L, D, I, M, L, lp, L, dp, dp, dp]
+        lib.oracle_cols.argtypes = [dp, dp, dp, dp, L, L, D, I, M, L, lp, L, dp, dp]
         for f in (lib.oracle_fwd, lib.oracle_bwd, lib.oracle_fwd_online, lib.oracle_rows,
                   lib.oracle_cols):
             f.restype = ctypes.c_int
@@ -68,6 +68,31 @@ def _heads(shape):
     return int(np.prod(shape[:-2], dtype=np.int64)), shape[-2], shape[-1]
 
 
+MASK_BLOCK = 128     # the block edge the kernels' masks use; the oracle takes any
+
+
+def _masks(block_mask, lead, N, block):
+    """Per-head uint8 [T, T] masks (T = ceil(N / block)) from None, one [T, T] mask for
+    every head, or masks with the inputs' leading dimensions: a list of nh arrays or None."""
+    nh = int(np.prod(lead, dtype=np.int64))
+    if block_mask is None:
+        return [None] * nh
+    m = block_mask.detach().cpu().numpy() if hasattr(block_mask, "detach") else np.asarray(block_mask)
+    m = (m != 0).astype(np.uint8)
+    T = (N + block - 1) // block
+    if m.shape == (T, T):
+        m = np.broadcast_to(m, (nh, T, T))
+    elif m.shape == tuple(lead) + (T, T):
+        m = m.reshape(nh, T, T)
+    else:
+        raise ValueError(f"block mask of shape {m.shape}, expected ({T}, {T}) or {tuple(lead) + (T, T)}")
+    return [np.ascontiguousarray(m[h]) for h in range(nh)]
+
+
+def _mp(m):
+    return None if m is None else m.ctypes.data_as(ctypes.c_void_p)
+
+
 def default_scale(d):
     """1/sqrt(d): 'IO-4 FlashAttention' problem setup; 'Flash Attention-3' code example."""
     return 1.0 / float(np.sqrt(d))
@@ -77,49 +102,53 @@ def num_threads():
     return _load().oracle_num_threads()
 
 
-def fwd(q, k, v, scale=None, causal=False):
+def fwd(q, k, v, scale=None, causal=False, block_mask=None, block=MASK_BLOCK):
     """Naive forward with explicit S and P.  Returns (O, LSE) as float64."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     nh, N, d = _heads(q.shape)
     if scale is None:
         scale = default_scale(d)
+    ms = _masks(block_mask, q.shape[:-2], N, block)
     qh, kh, vh = q.reshape(nh, N, d), k.reshape(nh, N, d), v.reshape(nh, N, d)
     O = np.empty((nh, N, d))
     LSE = np.empty((nh, N))
     for h in range(nh):
         _check(lib.oracle_fwd(_ptr(qh[h]), _ptr(kh[h]), _ptr(vh[h]), N, d, float(scale),
-                              int(bool(causal)), _ptr(O[h]), _ptr(LSE[h]), None), "oracle_fwd")
+                              int(bool(causal)), _mp(ms[h]), int(block), _ptr(O[h]), _ptr(LSE[h]), None),
+               "oracle_fwd")
     return O.reshape(q.shape), LSE.reshape(q.shape[:-1])
 
 
-def fwd_probs(q, k, v, scale=None, causal=False):
+def fwd_probs(q, k, v, scale=None, causal=False, block_mask=None, block=MASK_BLOCK):
     """Single head [N, d]: returns (O, LSE, P) with the explicit N x N P."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     N, d = q.shape
     if scale is None:
         scale = default_scale(d)
+    m = _masks(block_mask, (), N, block)[0]
     O, LSE, P = np.empty((N, d)), np.empty(N), np.empty((N, N))
-    _check(lib.oracle_fwd(_ptr(q), _ptr(k), _ptr(v), N, d, float(scale), int(bool(causal)),
+    _check(lib.oracle_fwd(_ptr(q), _ptr(k), _ptr(v), N, d, float(scale), int(bool(causal)), _mp(m), int(block),
                           _ptr(O), _ptr(LSE), _ptr(P)), "oracle_fwd")
     return O, LSE, P
 
 
-def bwd(q, k, v, do, scale=None, causal=False, return_D=False):
+def bwd(q, k, v, do, scale=None, causal=False, return_D=False, block_mask=None, block=MASK_BLOCK):
     """Naive backward.  Returns (dQ, dK, dV) [+ (D, D2) if return_D]."""
     lib = _load()
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     nh, N, d = _heads(q.shape)
     if scale is None:
         scale = default_scale(d)
+    ms = _masks(block_mask, q.shape[:-2], N, block)
     r = lambda a: a.reshape(nh, N, d)
     qh, kh, vh, gh = r(q), r(k), r(v), r(do)
     dQ, dK, dV = np.empty((nh, N, d)), np.empty((nh, N, d)), np.empty((nh, N, d))
     D, D2 = np.empty((nh, N)), np.empty((nh, N))
     for h in range(nh):
         _check(lib.oracle_bwd(_ptr(qh[h]), _ptr(kh[h]), _ptr(vh[h]), _ptr(gh[h]), N, d,
-                              float(scale), int(bool(causal)), _ptr(dQ[h]), _ptr(dK[h]),
+                              float(scale), int(bool(causal)), _mp(ms[h]), int(block), _ptr(dQ[h]), _ptr(dK[h]),
                               _ptr(dV[h]), _ptr(D[h]), _ptr(D2[h])), "oracle_bwd")
     out = (dQ.reshape(q.shape), dK.reshape(q.shape), dV.reshape(q.shape))
     if return_D:
@@ -127,24 +156,25 @@ def bwd(q, k, v, do, scale=None, causal=False, return_D=False):
     return out
 
 
-def fwd_online(q, k, v, scale=None, causal=False, Br=2, Bc=2):
+def fwd_online(q, k, v, scale=None, causal=False, Br=2, Bc=2, block_mask=None, block=MASK_BLOCK):
     """Forward by the tiled online recurrence.  Returns (O, LSE)."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     nh, N, d = _heads(q.shape)
     if scale is None:
         scale = default_scale(d)
+    ms = _masks(block_mask, q.shape[:-2], N, block)
     qh, kh, vh = q.reshape(nh, N, d), k.reshape(nh, N, d), v.reshape(nh, N, d)
     O = np.empty((nh, N, d))
     LSE = np.empty((nh, N))
     for h in range(nh):
         _check(lib.oracle_fwd_online(_ptr(qh[h]), _ptr(kh[h]), _ptr(vh[h]), N, d, float(scale),
-                                     int(bool(causal)), int(Br), int(Bc), _ptr(O[h]),
+                                     int(bool(causal)), _mp(ms[h]), int(block), int(Br), int(Bc), _ptr(O[h]),
                                      _ptr(LSE[h])), "oracle_fwd_online")
     return O.reshape(q.shape), LSE.reshape(q.shape[:-1])
 
 
-def rows(q, k, v, do, row_idx, scale=None, causal=False):
+def rows(q, k, v, do, row_idx, scale=None, causal=False, block_mask=None, block=MASK_BLOCK):
     """Single head [N, d]: (O, LSE, dQ) of the given query rows (dQ None if do is None)."""
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -156,13 +186,14 @@ def rows(q, k, v, do, row_idx, scale=None, causal=False):
     n = idx.shape[0]
     O, LSE = np.empty((n, d)), np.empty(n)
     dQ = None if do is None else np.empty((n, d))
+    m = _masks(block_mask, (), N, block)[0]
     _check(lib.oracle_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(do), N, d, float(scale),
-                           int(bool(causal)), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                           int(bool(causal)), _mp(m), int(block), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
                            n, _ptr(O), _ptr(LSE), _ptr(dQ)), "oracle_rows")
     return O, LSE, dQ
 
 
-def cols(q, k, v, do, col_idx, scale=None, causal=False):
+def cols(q, k, v, do, col_idx, scale=None, causal=False, block_mask=None, block=MASK_BLOCK):
     """Single head [N, d]: (dK, dV) of the given key rows."""
     lib = _load()
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
@@ -172,7 +203,8 @@ def cols(q, k, v, do, col_idx, scale=None, causal=False):
     idx = np.ascontiguousarray(np.asarray(col_idx, dtype=np.int64))
     n = idx.shape[0]
     dK, dV = np.empty((n, d)), np.empty((n, d))
+    m = _masks(block_mask, (), N, block)[0]
     _check(lib.oracle_cols(_ptr(q), _ptr(k), _ptr(v), _ptr(do), N, d, float(scale),
-                           int(bool(causal)), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                           int(bool(causal)), _mp(m), int(block), idx.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
                            n, _ptr(dK), _ptr(dV)), "oracle_cols")
     return dK, dV

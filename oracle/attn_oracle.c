@@ -14,6 +14,13 @@
  *                                        "Flash Attention-3" blog, code example
  *                                        (scale = d^-0.5, softmax over the last dim)
  *   causal: S_ij = -inf for key j > query i   (the plainest reading; not on the pages)
+ *   block mask (optional): S_ij = -inf where entry (i / block, j / block) of a
+ *     T x T byte mask is zero, T = ceil(N / block)
+ *                                        FlashAttention-2 review, 'sparse/hybrid'
+ *                                        answer, section 3 (1) (Sparse FlashAttention:
+ *                                        only the important blocks are computed)
+ *   a row with no kept key: P_i = 0, O_i = 0, LSE_i = log(0) = -inf, and it
+ *   adds nothing to any gradient (the empty sum; the pages never meet the case)
  *   P = softmax(S) row-wise, O = P V     FlashAttention-2 review, "core algorithm"
  *                                        answer, section 1 (basic operation)
  *   LSE_i = m_i + ln(l_i)                the saved row statistic (m, l) of the same
@@ -47,7 +54,24 @@
 #include <omp.h>
 #endif
 
-static int allowed(long i, long j, int causal) { return !causal || j <= i; }
+/* The keys each query attends to. */
+typedef struct {
+    int causal;
+    const unsigned char* bmask;   /* NULL: no block mask */
+    long block, nblk;             /* block edge, blocks per side */
+} keyset;
+
+static keyset make_keyset(long N, int causal, const unsigned char* bmask, long block)
+{
+    keyset ks = {causal, bmask, block, bmask ? (N + block - 1) / block : 0};
+    return ks;
+}
+
+static int allowed(const keyset* ks, long i, long j)
+{
+    if (ks->causal && j > i) return 0;
+    return !ks->bmask || ks->bmask[(i / ks->block) * ks->nblk + j / ks->block] != 0;
+}
 
 static double dot(const double* a, const double* b, long d)
 {
@@ -56,9 +80,9 @@ static double dot(const double* a, const double* b, long d)
     return s;
 }
 
-static int bad_args(long N, long d, double scale, int causal)
+static int bad_args(long N, long d, double scale, int causal, const unsigned char* bmask, long block)
 {
-    return N < 1 || d < 1 || !isfinite(scale) || (causal != 0 && causal != 1);
+    return N < 1 || d < 1 || !isfinite(scale) || (causal != 0 && causal != 1) || (bmask && block < 1);
 }
 
 int oracle_num_threads(void)
@@ -73,9 +97,11 @@ int oracle_num_threads(void)
 /* Naive forward with explicit S and P (N x N).  P_out (optional, N x N)
  * receives P.  O: N x d, LSE: N. */
 int oracle_fwd(const double* Q, const double* K, const double* V, long N, long d,
-               double scale, int causal, double* O, double* LSE, double* P_out)
+               double scale, int causal, const unsigned char* bmask, long block,
+               double* O, double* LSE, double* P_out)
 {
-    if (!Q || !K || !V || !O || !LSE || bad_args(N, d, scale, causal)) return -1;
+    if (!Q || !K || !V || !O || !LSE || bad_args(N, d, scale, causal, bmask, block)) return -1;
+    const keyset ks = make_keyset(N, causal, bmask, block);
     double* S = (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
     double* P = P_out ? P_out : (double*)malloc(sizeof(double) * (size_t)N * (size_t)N);
     if (!S || !P) { free(S); if (!P_out) free(P); return -2; }
@@ -84,7 +110,7 @@ int oracle_fwd(const double* Q, const double* K, const double* V, long N, long d
 #pragma omp parallel for schedule(dynamic, 4)
     for (long i = 0; i < N; ++i)
         for (long j = 0; j < N; ++j)
-            S[i * N + j] = allowed(i, j, causal) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
+            S[i * N + j] = allowed(&ks, i, j) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
 
     /* P = softmax(S) row-wise; LSE = m + ln l */
 #pragma omp parallel for schedule(dynamic, 4)
@@ -119,10 +145,10 @@ int oracle_fwd(const double* Q, const double* K, const double* V, long N, long d
  * D_i = sum_j P_ij dP_ij and D2_out (optional, N) receives the same quantity as
  * sum_k dO_ik O_ik, so that a caller can check the two are equal. */
 int oracle_bwd(const double* Q, const double* K, const double* V, const double* dO,
-               long N, long d, double scale, int causal,
+               long N, long d, double scale, int causal, const unsigned char* bmask, long block,
                double* dQ, double* dK, double* dV, double* D_out, double* D2_out)
 {
-    if (!Q || !K || !V || !dO || !dQ || !dK || !dV || bad_args(N, d, scale, causal)) return -1;
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV || bad_args(N, d, scale, causal, bmask, block)) return -1;
     size_t nn = (size_t)N * (size_t)N;
     double* P = (double*)malloc(sizeof(double) * nn);
     double* dS = (double*)malloc(sizeof(double) * nn);
@@ -131,7 +157,7 @@ int oracle_bwd(const double* Q, const double* K, const double* V, const double* 
     double* D = (double*)malloc(sizeof(double) * (size_t)N);
     int rc = -2;
     if (!P || !dS || !O || !LSE || !D) goto out;
-    rc = oracle_fwd(Q, K, V, N, d, scale, causal, O, LSE, P);
+    rc = oracle_fwd(Q, K, V, N, d, scale, causal, bmask, block, O, LSE, P);
     if (rc) goto out;
 
     /* dP = dO V^T (stored in dS for now), D_i = sum_j P_ij dP_ij */
@@ -192,9 +218,12 @@ out:
  * l = alpha l + rowsum exp(S_blk - m');  acc = alpha acc + exp(S_blk - m') V_blk;
  * m = m'.  At the end O = acc / l and LSE = m + ln l. */
 int oracle_fwd_online(const double* Q, const double* K, const double* V, long N, long d,
-                      double scale, int causal, long Br, long Bc, double* O, double* LSE)
+                      double scale, int causal, const unsigned char* bmask, long block,
+                      long Br, long Bc, double* O, double* LSE)
 {
-    if (!Q || !K || !V || !O || !LSE || bad_args(N, d, scale, causal) || Br < 1 || Bc < 1) return -1;
+    if (!Q || !K || !V || !O || !LSE || bad_args(N, d, scale, causal, bmask, block) || Br < 1 || Bc < 1)
+        return -1;
+    const keyset ks = make_keyset(N, causal, bmask, block);
     long Tr = (N + Br - 1) / Br;
     int rc = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -220,7 +249,7 @@ int oracle_fwd_online(const double* Q, const double* K, const double* V, long N,
                 double rowmax = -INFINITY;
                 for (long c = 0; c < nc; ++c) {
                     long j = c0 + c;
-                    s[c] = allowed(i, j, causal) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
+                    s[c] = allowed(&ks, i, j) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
                     if (s[c] > rowmax) rowmax = s[c];
                 }
                 double mnew = m[r] > rowmax ? m[r] : rowmax;
@@ -239,7 +268,8 @@ int oracle_fwd_online(const double* Q, const double* K, const double* V, long N,
             }
         }
         for (long r = 0; r < nr; ++r) {
-            for (long k = 0; k < d; ++k) O[(r0 + r) * d + k] = acc[r * d + k] / l[r];
+            /* a row that kept no key stays at acc = 0, l = 0: O = 0 */
+            for (long k = 0; k < d; ++k) O[(r0 + r) * d + k] = l[r] > 0.0 ? acc[r * d + k] / l[r] : 0.0;
             LSE[r0 + r] = m[r] + log(l[r]);
         }
         free(m); free(l); free(acc); free(Sb);
@@ -251,10 +281,11 @@ int oracle_fwd_online(const double* Q, const double* K, const double* V, long N,
  * O, LSE and dQ of rows[0..nrows).  O_rows, dQ_rows: nrows x d; LSE_rows: nrows.
  * dO and dQ_rows may both be NULL to skip the gradient. */
 int oracle_rows(const double* Q, const double* K, const double* V, const double* dO,
-                long N, long d, double scale, int causal, const long* rows, long nrows,
-                double* O_rows, double* LSE_rows, double* dQ_rows)
+                long N, long d, double scale, int causal, const unsigned char* bmask, long block,
+                const long* rows, long nrows, double* O_rows, double* LSE_rows, double* dQ_rows)
 {
-    if (!Q || !K || !V || !rows || !O_rows || !LSE_rows || bad_args(N, d, scale, causal)) return -1;
+    if (!Q || !K || !V || !rows || !O_rows || !LSE_rows || bad_args(N, d, scale, causal, bmask, block)) return -1;
+    const keyset ks = make_keyset(N, causal, bmask, block);
     if ((dO == NULL) != (dQ_rows == NULL)) return -1;
     for (long t = 0; t < nrows; ++t) if (rows[t] < 0 || rows[t] >= N) return -1;
     int rc = 0;
@@ -269,7 +300,7 @@ int oracle_rows(const double* Q, const double* K, const double* V, const double*
         }
         double m = -INFINITY;
         for (long j = 0; j < N; ++j) {
-            s[j] = allowed(i, j, causal) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
+            s[j] = allowed(&ks, i, j) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
             if (s[j] > m) m = s[j];
         }
         double l = 0.0;
@@ -302,10 +333,12 @@ int oracle_rows(const double* Q, const double* K, const double* V, const double*
  * cols[0..ncols).  Every query row's LSE_i and D_i = dO_i . O_i is computed
  * first (row by row, as in oracle_rows), then P_ij = exp(S_ij - LSE_i). */
 int oracle_cols(const double* Q, const double* K, const double* V, const double* dO,
-                long N, long d, double scale, int causal, const long* cols, long ncols,
-                double* dK_cols, double* dV_cols)
+                long N, long d, double scale, int causal, const unsigned char* bmask, long block,
+                const long* cols, long ncols, double* dK_cols, double* dV_cols)
 {
-    if (!Q || !K || !V || !dO || !cols || !dK_cols || !dV_cols || bad_args(N, d, scale, causal)) return -1;
+    if (!Q || !K || !V || !dO || !cols || !dK_cols || !dV_cols || bad_args(N, d, scale, causal, bmask, block))
+        return -1;
+    const keyset ks = make_keyset(N, causal, bmask, block);
     for (long t = 0; t < ncols; ++t) if (cols[t] < 0 || cols[t] >= N) return -1;
     double* LSE = (double*)malloc(sizeof(double) * (size_t)N);
     double* D = (double*)malloc(sizeof(double) * (size_t)N);
@@ -322,7 +355,7 @@ int oracle_cols(const double* Q, const double* K, const double* V, const double*
         double* o = s + N;
         double m = -INFINITY;
         for (long j = 0; j < N; ++j) {
-            s[j] = allowed(i, j, causal) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
+            s[j] = allowed(&ks, i, j) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;
             if (s[j] > m) m = s[j];
         }
         double l = 0.0;
@@ -345,7 +378,7 @@ int oracle_cols(const double* Q, const double* K, const double* V, const double*
         double* gv = dV_cols + t * d;
         for (long k = 0; k < d; ++k) { gk[k] = 0.0; gv[k] = 0.0; }
         for (long i = 0; i < N; ++i) {
-            if (!allowed(i, j, causal)) continue;
+            if (!allowed(&ks, i, j)) continue;
             double p = exp(scale * dot(Q + i * d, K + j * d, d) - LSE[i]);
             double ds = p * (dot(dO + i * d, V + j * d, d) - D[i]);
             for (long k = 0; k < d; ++k) {

@@ -77,6 +77,25 @@ def test_bwd_rejects_before_launch():
     assert L.attn_bwd_dq(P, P, P, P, P, NUL, attn.ATTN_BF16, 1, 1, 16, 64, 0.1, 0, P, None) == attn.ATTN_EINVAL
 
 
+def test_blocksparse_rejects_bad_masks_before_launch():
+    L = attn.lib()
+    M = ctypes.c_void_p(0x20001)           # byte mask: no alignment needed, never read here
+    fwd = lambda mask=M, heads=1, B=2, H=3, d=64, **kw: L.attn_fwd_blocksparse(
+        P, P, P, attn.ATTN_BF16, B, H, 300, d, 0.125, kw.get("causal", 1), mask, heads, P, P, None)
+    assert fwd(mask=NUL) == attn.ATTN_EINVAL
+    assert fwd(heads=0) == attn.ATTN_EINVAL
+    assert fwd(heads=5) == attn.ATTN_EINVAL                  # neither 1 nor B*H = 6
+    assert fwd(heads=6, d=96) == attn.ATTN_EUNSUPPORTED
+    assert fwd(heads=6, causal=2) == attn.ATTN_EINVAL
+    ws = L.attn_bwd_workspace_bytes(2, 3, 300, 64)
+    bwd = lambda mask=M, heads=1, wsb=ws: L.attn_bwd_blocksparse(
+        P, P, P, P, P, P, attn.ATTN_BF16, 2, 3, 300, 64, 0.125, 0, mask, heads, P, P, P, attn.ATTN_F32, P,
+        ctypes.c_size_t(wsb), None)
+    assert bwd(mask=NUL) == attn.ATTN_EINVAL
+    assert bwd(heads=7) == attn.ATTN_EINVAL
+    assert bwd(heads=6, wsb=ws - 1) == attn.ATTN_EINVAL
+
+
 def test_workspace_sizes():
     L = attn.lib()
     rows = 4 * 16 * 4096

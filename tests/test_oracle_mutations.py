@@ -19,10 +19,10 @@ PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
 
 # (name, text in the source, replacement): each text occurs exactly once
 MUTATIONS = [
-    ("causal mask admits the diagonal only after it", "return !causal || j <= i;", "return !causal || j < i;"),
+    ("causal mask excludes the diagonal", "if (ks->causal && j > i) return 0;", "if (ks->causal && j >= i) return 0;"),
     ("scale dropped from S (naive forward)",
-     "S[i * N + j] = allowed(i, j, causal) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;",
-     "S[i * N + j] = allowed(i, j, causal) ? dot(Q + i * d, K + j * d, d) : -INFINITY;"),
+     "S[i * N + j] = allowed(&ks, i, j) ? scale * dot(Q + i * d, K + j * d, d) : -INFINITY;",
+     "S[i * N + j] = allowed(&ks, i, j) ? dot(Q + i * d, K + j * d, d) : -INFINITY;"),
     ("softmax not normalised",
      "P[i * N + j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m) / l;",
      "P[i * N + j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);"),
@@ -45,8 +45,13 @@ MUTATIONS = [
      "            double s = dS[i * N + j], p = P[i * N + j];\n            for (long k = 0; k < d; ++k) {\n"
      "                gk[k] += s * Q[i * d + k];\n                gv[k] += p * dO[j * d + k];"),
     ("online rescale factor inverted", "exp(m[r] - mnew);", "exp(mnew - m[r]);"),
-    ("online forward without the final division", "O[(r0 + r) * d + k] = acc[r * d + k] / l[r];",
-     "O[(r0 + r) * d + k] = acc[r * d + k];"),
+    ("online forward without the final division", "l[r] > 0.0 ? acc[r * d + k] / l[r] : 0.0;",
+     "l[r] > 0.0 ? acc[r * d + k] : 0.0;"),
+    ("block mask indexed transposed", "ks->bmask[(i / ks->block) * ks->nblk + j / ks->block]",
+     "ks->bmask[(j / ks->block) * ks->nblk + i / ks->block]"),
+    ("block mask ignored", "return !ks->bmask || ks->bmask[", "return 1 || ks->bmask["),
+    ("online forward: empty rows divided by zero", "l[r] > 0.0 ? acc[r * d + k] / l[r] : 0.0;",
+     "acc[r * d + k] / l[r];"),
     ("rows: D_i left out of dS", "double D = dot(g, o, d);", "double D = 0.0;"),
     ("cols: P normalised by the key's statistic", "K + j * d, d) - LSE[i]);", "K + j * d, d) - LSE[j]);"),
 ]

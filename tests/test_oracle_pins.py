@@ -289,3 +289,181 @@ def test_bad_arguments_rejected():
         oracle.fwd(q, q, q, scale=float("nan"))
     with pytest.raises(RuntimeError):
         oracle.rows(q, q, q, None, [4])
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse masks: FlashAttention-2 review, 'sparse/hybrid' answer,
+# section 3 (1) -- only the kept blocks of the score matrix are computed.
+# Special cases that reduce to dense attention on smaller problems, the
+# online recurrence, and finite differences.
+# ---------------------------------------------------------------------------
+def _mask(T, density, seed, empty_rows=()):
+    m = (np.random.default_rng(seed).random((T, T)) < density).astype(np.uint8)
+    for a in empty_rows:
+        m[a] = 0
+    return m
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_all_kept_is_dense(causal):
+    N, d, blk = 23, 5, 4
+    q, k, v, do = _rand(2, N, d), _rand(2, N, d), _rand(2, N, d), _rand(2, N, d)
+    T = (N + blk - 1) // blk
+    ones = np.ones((T, T), np.uint8)
+    np.testing.assert_array_equal(oracle.fwd(q, k, v, causal=causal, block_mask=ones, block=blk)[0],
+                                  oracle.fwd(q, k, v, causal=causal)[0])
+    for a, b in zip(oracle.bwd(q, k, v, do, causal=causal, block_mask=ones, block=blk),
+                    oracle.bwd(q, k, v, do, causal=causal)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_mask_lower_triangle_with_causal_is_causal():
+    """A block mask that keeps the blocks on and below the diagonal changes nothing under causal."""
+    N, d, blk = 21, 4, 3
+    q, k, v, do = _rand(N, d), _rand(N, d), _rand(N, d), _rand(N, d)
+    T = (N + blk - 1) // blk
+    tri = np.tril(np.ones((T, T), np.uint8))
+    O1, L1 = oracle.fwd(q, k, v, causal=True, block_mask=tri, block=blk)
+    O2, L2 = oracle.fwd(q, k, v, causal=True)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(L1, L2)
+    # without causal the same mask is a different (block-causal) problem
+    O3, _ = oracle.fwd(q, k, v, causal=False, block_mask=tri, block=blk)
+    assert np.abs(O3 - O2).max() > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_block_diagonal_is_independent_segments(causal):
+    """A block-diagonal mask splits the sequence into independent attention problems."""
+    N, d, blk = 26, 6, 5
+    q, k, v, do = _rand(N, d), _rand(N, d), _rand(N, d), _rand(N, d)
+    T = (N + blk - 1) // blk
+    eye = np.eye(T, dtype=np.uint8)
+    O, L = oracle.fwd(q, k, v, causal=causal, block_mask=eye, block=blk)
+    dQ, dK, dV = oracle.bwd(q, k, v, do, causal=causal, block_mask=eye, block=blk)
+    for a in range(T):
+        r = slice(a * blk, min(N, (a + 1) * blk))
+        Os, Ls = oracle.fwd(q[r], k[r], v[r], causal=causal)
+        gs = oracle.bwd(q[r], k[r], v[r], do[r], causal=causal)
+        np.testing.assert_allclose(O[r], Os, atol=1e-13)
+        np.testing.assert_allclose(L[r], Ls, atol=1e-13)
+        for full, seg in zip((dQ, dK, dV), gs):
+            np.testing.assert_allclose(full[r], seg, atol=1e-13)
+
+
+def test_mask_one_block_per_row_is_dense_on_that_block():
+    """Query block a keeps only key block pi(a): dense attention of Q_a on K_pi(a), V_pi(a)."""
+    N, d, blk = 24, 4, 6
+    q, k, v = _rand(N, d), _rand(N, d), _rand(N, d)
+    T = N // blk
+    pi = [2, 0, 3, 1]
+    m = np.zeros((T, T), np.uint8)
+    for a in range(T):
+        m[a, pi[a]] = 1
+    O, L = oracle.fwd(q, k, v, block_mask=m, block=blk)
+    for a in range(T):
+        r, c = slice(a * blk, (a + 1) * blk), slice(pi[a] * blk, (pi[a] + 1) * blk)
+        # P_a = softmax(scale q_a k_c^T): the dense oracle on a problem whose keys are block c
+        Os, Ls = oracle.fwd(q[r], k[c], v[c])
+        np.testing.assert_allclose(O[r], Os, atol=1e-13)
+        np.testing.assert_allclose(L[r], Ls, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_empty_rows(causal):
+    """A query block that keeps no key: O = 0, LSE = -inf, dQ = 0, and it adds nothing to dK, dV."""
+    N, d, blk = 20, 4, 4
+    q, k, v, do = _rand(N, d), _rand(N, d), _rand(N, d), _rand(N, d)
+    T = N // blk
+    m = _mask(T, 0.6, 3, empty_rows=(2,))
+    m[np.arange(T), np.arange(T)] = 1
+    m[2] = 0
+    O, L = oracle.fwd(q, k, v, causal=causal, block_mask=m, block=blk)
+    r = slice(8, 12)
+    assert np.all(O[r] == 0.0) and np.all(np.isneginf(L[r]))
+    dQ, dK, dV = oracle.bwd(q, k, v, do, causal=causal, block_mask=m, block=blk)
+    assert np.all(dQ[r] == 0.0)
+    # the empty rows add nothing to dK, dV: zeroing their dO changes nothing
+    do0 = do.copy()
+    do0[r] = 0.0
+    _, dK0, dV0 = oracle.bwd(q, k, v, do0, causal=causal, block_mask=m, block=blk)
+    np.testing.assert_array_equal(dK, dK0)
+    np.testing.assert_array_equal(dV, dV0)
+    # the other rows are those of the same mask with the empty block row kept on its diagonal
+    m2 = m.copy()
+    m2[2, 2] = 1
+    O2, L2 = oracle.fwd(q, k, v, causal=causal, block_mask=m2, block=blk)
+    keep = np.r_[0:8, 12:N]
+    np.testing.assert_array_equal(O2[keep], O[keep])
+    np.testing.assert_array_equal(L2[keep], L[keep])
+    assert np.isfinite(L2[r]).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("blocks", [(1, 1), (3, 2), (4, 4)])
+def test_mask_online_recurrence_matches_naive(causal, blocks):
+    """The tiled online recurrence under a mask (with an empty query block) equals the explicit softmax."""
+    N, d, blk = 22, 5, 4
+    q, k, v = _rand(N, d), _rand(N, d), _rand(N, d)
+    T = (N + blk - 1) // blk
+    m = _mask(T, 0.5, 11, empty_rows=(1,))
+    O1, L1 = oracle.fwd(q, k, v, causal=causal, block_mask=m, block=blk)
+    O2, L2 = oracle.fwd_online(q, k, v, causal=causal, Br=blocks[0], Bc=blocks[1], block_mask=m, block=blk)
+    assert np.isfinite(O2).all()
+    np.testing.assert_allclose(O2, O1, rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(L2), np.isneginf(L1))
+    fin = np.isfinite(L1)
+    np.testing.assert_allclose(L2[fin], L1[fin], rtol=1e-14, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_backward_finite_differences(causal):
+    """Central differences of L = sum(dO o O) under a block mask with an empty block row."""
+    N, d, s, h, blk = 8, 3, 0.9, 1e-5, 2
+    q, k, v, do = _rand(N, d), _rand(N, d), _rand(N, d), _rand(N, d)
+    m = np.array([[1, 0, 1, 0], [0, 0, 0, 0], [1, 1, 0, 1], [0, 1, 1, 1]], np.uint8)
+    dQ, dK, dV = oracle.bwd(q, k, v, do, scale=s, causal=causal, block_mask=m, block=blk)
+
+    def loss(qq, kk, vv):
+        O, _ = oracle.fwd(qq, kk, vv, scale=s, causal=causal, block_mask=m, block=blk)
+        return float((O * do).sum())
+
+    for name, x, g in (("q", q, dQ), ("k", k, dK), ("v", v, dV)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"])
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_rows_and_cols_match_full(causal):
+    N, d, blk = 40, 6, 8
+    q, k, v, do = _rand(N, d), _rand(N, d), _rand(N, d), _rand(N, d)
+    T = N // blk
+    m = _mask(T, 0.5, 5, empty_rows=(3,))
+    O, L = oracle.fwd(q, k, v, causal=causal, block_mask=m, block=blk)
+    dQ, dK, dV = oracle.bwd(q, k, v, do, causal=causal, block_mask=m, block=blk)
+    idx = [0, 9, 25, 39, 17, 30]
+    Or, Lr, dQr = oracle.rows(q, k, v, do, idx, causal=causal, block_mask=m, block=blk)
+    np.testing.assert_allclose(Or, O[idx], atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(Lr), np.isneginf(L[idx]))
+    fin = np.isfinite(L[idx])
+    np.testing.assert_allclose(Lr[fin], L[idx][fin], atol=1e-13)
+    np.testing.assert_allclose(dQr, dQ[idx], atol=1e-13)
+    dKc, dVc = oracle.cols(q, k, v, do, idx, causal=causal, block_mask=m, block=blk)
+    np.testing.assert_allclose(dKc, dK[idx], atol=1e-13)
+    np.testing.assert_allclose(dVc, dV[idx], atol=1e-13)
+
+
+def test_mask_shape_checked():
+    q = np.zeros((10, 2))
+    with pytest.raises(ValueError):
+        oracle.fwd(q, q, q, block_mask=np.ones((2, 2)), block=4)       # T = 3
