@@ -4,7 +4,8 @@ One step = forward (attn_fwd) + backward preprocess (attn_bwd_preprocess) +
 key-side backward (attn_bwd_dkdv) + query-side backward (attn_bwd_dq) over one
 batch of resident synthetic inputs: the whole path, fwd and bwd.  Default workload: B=4, H=16, N=4096,
 d=128, causal, bf16 (the N = 4k case of the headline metric); the N = 16k case
-(B=1, H=16) is measured in the same run and reported under "secondary".
+(B=1, H=16) is measured in the same run and reported under "secondary", and the
+same N = 16k shape with a local + global block mask under "block_sparse".
 
 Prints ONE JSON line.  `value` is fwd+bwd TFLOP/s (4 N^2 d per head forward,
 2.5x that backward, halved for the causal mask) from the wall clock around
@@ -23,10 +24,11 @@ sys.path.insert(0, ROOT)
 
 import torch  # noqa: E402
 
-from exact_tiled_attention_12_amd import attn_bwd_dkdv, attn_bwd_dq, attn_bwd_preprocess, attn_fwd  # noqa: E402
+from exact_tiled_attention_12_amd import (attn_bwd_blocksparse, attn_bwd_dkdv, attn_bwd_dq,  # noqa: E402
+                                          attn_bwd_preprocess, attn_fwd, attn_fwd_blocksparse)
 from exact_tiled_attention_12_amd.configs import CONFIGS  # noqa: E402
-from exact_tiled_attention_12_amd.flops import attn_flops  # noqa: E402
-from exact_tiled_attention_12_amd.inputs import config_inputs  # noqa: E402
+from exact_tiled_attention_12_amd.flops import attn_flops, blocksparse_flops  # noqa: E402
+from exact_tiled_attention_12_amd.inputs import config_inputs, local_global_mask  # noqa: E402
 
 METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=4k/16k, d=128"
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA, published
@@ -101,6 +103,61 @@ class Workload:
         return wall, per
 
 
+class SparseWorkload:
+    """Workload 4's shape (B=1 H=16 N=16384 d=128 causal) under a local + global block
+    mask: each 128-query block keeps the key blocks within `window` blocks of its own
+    and the first `n_global` ones.  One step = attn_fwd_blocksparse + attn_bwd_blocksparse."""
+
+    def __init__(self, cfg, dev, window=8, n_global=1):
+        self.cfg = cfg
+        q, k, v, do = config_inputs(cfg)
+        self.q, self.k, self.v, self.do = (t.to(dev) for t in (q, k, v, do))
+        B, H, N, d = q.shape
+        T = (N + 127) // 128
+        self.mask_cpu = local_global_mask(T, window, n_global)
+        self.mask = self.mask_cpu.to(dev)
+        self.desc = (f"B={B} H={H} N={N} d={d} causal bf16, block mask: local {window} blocks + "
+                     f"{n_global} global (128-row blocks), {int(self.mask_cpu.sum())} of {T * T} blocks kept")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(B * H * N * 4 + 256, dtype=torch.uint8, device=dev)
+        self.dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+        self.dk = torch.empty_like(self.dq)
+        self.dv = torch.empty_like(self.dq)
+        self.fl_fwd = B * H * blocksparse_flops(self.mask_cpu, N, d, cfg.causal, "fwd")
+        self.fl_bwd = 2.5 * self.fl_fwd
+        self.fl_dense = attn_flops(B, H, N, d, cfg.causal, "fwd+bwd")
+
+    def step(self, ev=None):
+        c = self.cfg
+        if ev is not None:
+            ev[0].record()
+        attn_fwd_blocksparse(self.q, self.k, self.v, self.mask, causal=c.causal, out=self.o, lse=self.lse)
+        if ev is not None:
+            ev[1].record()
+        attn_bwd_blocksparse(self.q, self.k, self.v, self.o, self.do, self.lse, self.mask, causal=c.causal,
+                             workspace=self.ws, dq=self.dq, dk=self.dk, dv=self.dv)
+        if ev is not None:
+            ev[2].record()
+
+    def measure(self, steps, warmup):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in evs:
+            self.step(e)
+        torch.cuda.synchronize()
+        t_fwd = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e-3
+        t_bwd = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e-3
+        return wall, t_fwd, t_bwd
+
+
 def cpu_baseline(cfg, budget_s=12.0):
     """The fp64 oracle (as it stands) on whole heads of the same workload, fwd + bwd."""
     import oracle
@@ -143,6 +200,9 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-secondary", action="store_true", help="skip the N=16k measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse measurement")
+    ap.add_argument("--sparse-only", action="store_true",
+                    help="only the block-sparse measurement (prints its JSON object; for profiling)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a plain 1 GiB device copy (rocprofv3 counter calibration)")
     args = ap.parse_args()
@@ -163,6 +223,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": a.numel(), "launches": 3}))
+        return
+
+    if args.sparse_only:
+        ws = SparseWorkload(CONFIGS[4], dev)
+        log(f"bench: block-sparse, {ws.desc}")
+        wall_s, tf_s, tb_s = ws.measure(args.steps, args.warmup)
+        log(f"bench: block-sparse step {wall_s * 1e3:.3f} ms; fwd {tf_s * 1e6:.1f} us, bwd {tb_s * 1e6:.1f} us")
+        print(json.dumps({"block_sparse_ms_per_step": round(wall_s * 1e3, 4), "fwd_us": round(tf_s * 1e6, 2),
+                          "bwd_us": round(tb_s * 1e6, 2)}), flush=True)
         return
 
     cfg = CONFIGS[args.config]
@@ -233,6 +302,22 @@ def main():
             "kernels_us": {n: round(t * 1e6, 2) for n, t in per4.items()},
         }
         log(f"bench: N=16384 step {wall4 * 1e3:.3f} ms; " + ", ".join(f"{n} {t * 1e6:.1f} us" for n, t in per4.items()))
+
+    if cfg.index == 3 and not args.no_sparse:
+        torch.cuda.empty_cache()
+        ws = SparseWorkload(CONFIGS[4], dev)
+        log(f"bench: block-sparse, {ws.desc}")
+        steps_s = max(3, args.steps // 2)
+        wall_s, tf_s, tb_s = ws.measure(steps_s, max(2, args.warmup // 2))
+        out["block_sparse"] = {
+            "workload": ws.desc, "steps": steps_s, "ms_per_step": round(wall_s * 1e3, 4),
+            "value": round((ws.fl_fwd + ws.fl_bwd) / wall_s / 1e12, 2), "unit": "TFLOP/s (kept pairs)",
+            "fwd_us": round(tf_s * 1e6, 2), "bwd_us": round(tb_s * 1e6, 2),
+            "fwd_tflops": round(ws.fl_fwd / tf_s / 1e12, 2),
+            "bwd_tflops": round(ws.fl_bwd / tb_s / 1e12, 2),
+            "kept_fraction_of_causal_flops": round((ws.fl_fwd + ws.fl_bwd) / ws.fl_dense, 4),
+        }
+        log(f"bench: block-sparse step {wall_s * 1e3:.3f} ms; fwd {tf_s * 1e6:.1f} us, bwd {tb_s * 1e6:.1f} us")
 
     if not args.no_cpu:
         log("bench: CPU oracle baseline")
