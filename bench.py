@@ -35,6 +35,7 @@ PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 KERNEL_SOURCES = ["exact_tiled_attention_12_amd/csrc/attn_fwd.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_bwd.hip",
+                  "exact_tiled_attention_12_amd/csrc/attn_fwd_fp8.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_common.h"]
 
 

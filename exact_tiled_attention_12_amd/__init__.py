@@ -5,6 +5,6 @@ include/attn.h); this package holds its ctypes binding, the autograd wrapper, th
 workload shapes, the seeded input generator and the FLOP accounting.
 """
 from .attn import (attn_bwd, attn_bwd_blocksparse, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_main,  # noqa: F401
-                   attn_bwd_preprocess, attn_bwd_workspace_bytes, attn_fwd, attn_fwd_blocksparse, lib,
+                   attn_bwd_preprocess, attn_bwd_workspace_bytes, attn_fwd, attn_fwd_blocksparse, attn_fwd_fp8, lib,
                    AttnError, LIB_PATH, MASK_BLOCK)
 from .autograd import FlashAttentionFn, flash_attention  # noqa: F401

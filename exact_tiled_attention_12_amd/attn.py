@@ -20,7 +20,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
             "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
-            "attn_status_str", "attn_last_hip_error")
+            "attn_fwd_fp8", "attn_status_str", "attn_last_hip_error")
 MASK_BLOCK = 128        # ATTN_MASK_BLOCK: rows and keys per block-mask entry
 
 _lib = None
@@ -54,8 +54,9 @@ def lib():
         L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, vp]
         L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, vp, i, vp,
                                            sz, vp]
+        L.attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, i, i, i, i, f, i, vp, vp, vp]
         for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
-                     "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse"):
+                     "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse", "attn_fwd_fp8"):
             getattr(L, name).restype = i
         L.attn_status_str.argtypes = [i]
         L.attn_status_str.restype = ctypes.c_char_p
@@ -244,3 +245,22 @@ def attn_bwd_blocksparse(q, k, v, o, do, lse, block_mask, scale=None, causal=Fal
           float(scale), int(bool(causal)), _ptr(m), heads, _ptr(dq), _ptr(dk), _ptr(dv), gdt, _ptr(workspace),
           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q, stream))
     return dq, dk, dv
+
+
+def attn_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal=False, out=None, lse=None,
+                 stream=None):
+    """Forward on fp8 e4m3 inputs (torch.float8_e4m3fn, [B, H, N, d], d = 64 or 128) whose real values are
+    descale * tensor.  Returns (O in bf16, LSE in fp32)."""
+    B, H, N, d = _shape(q8)
+    for t in (q8, k8, v8):
+        if t.dtype != torch.float8_e4m3fn or t.shape != q8.shape:
+            raise ValueError("q8, k8, v8 must be float8_e4m3fn tensors of one shape")
+    _check_inputs(q8, k8, v8)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _check_inputs(q8, o, l)
+    _call("attn_fwd_fp8", _ptr(q8), _ptr(k8), _ptr(v8), float(q_descale), float(k_descale), float(v_descale),
+          B, H, N, d, float(scale), int(bool(causal)), _ptr(o), _ptr(l), _stream(q8, stream))
+    return o, l

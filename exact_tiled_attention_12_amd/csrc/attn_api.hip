@@ -169,6 +169,21 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                    workspace_bytes, stream);
 }
 
+attn_status attn_fwd_fp8(const void* Q, const void* K, const void* V, float q_descale, float k_descale,
+                         float v_descale, int B, int H, int N, int d, float scale, int causal, void* O, float* LSE,
+                         void* stream)
+{
+    attn_status s = check_shape(B, H, N, d);
+    if (s != ATTN_OK) return s;
+    if (d == 80) return ATTN_EUNSUPPORTED;
+    if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale) ||
+        (causal != 0 && causal != 1))
+        return ATTN_EINVAL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return ATTN_EINVAL;
+    return from_hip(attn::launch_fwd_fp8(Q, K, V, q_descale, k_descale, v_descale, O, LSE, B * H, N, d, scale, causal,
+                                         (hipStream_t)stream));
+}
+
 // bytes between the masks of consecutive heads, or -1 for a bad mask argument
 static long mask_head_stride(const unsigned char* block_mask, int mask_heads, int B, int H, int N)
 {

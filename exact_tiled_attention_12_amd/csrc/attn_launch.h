@@ -32,6 +32,11 @@ hipError_t launch_bwd_f32(const void* Q, const void* K, const void* V, const voi
                           const float* D, int BH, int N, int d, float scale, int causal, float* dQacc, float* dK,
                           float* dV, const uint8_t* bmask, long mhead, hipStream_t st);
 
+// fp8 e4m3 inputs with per-tensor dequantisation factors; O in bf16 (d = 64 or 128).
+hipError_t launch_fwd_fp8(const void* Q, const void* K, const void* V, float q_descale, float k_descale,
+                          float v_descale, void* O, float* LSE, int BH, int N, int d, float scale, int causal,
+                          hipStream_t st);
+
 hipError_t launch_f32_to_bf16(const float* src, void* dst, long n, hipStream_t st);
 
 }  // namespace attn

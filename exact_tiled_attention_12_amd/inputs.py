@@ -52,3 +52,22 @@ def local_global_mask(T, window, n_global):
     a = torch.arange(T).view(T, 1)
     b = torch.arange(T).view(1, T)
     return (((a - b).abs() < window) | (b < n_global)).to(torch.uint8)
+
+
+FP8_MAX = 448.0        # largest finite OCP e4m3 ("e4m3fn") value
+
+
+def make_fp8_inputs(B, H, N, d, seed=0):
+    """fp8 e4m3 inputs with per-tensor dequantisation factors: i.i.d. N(0, 1) draws
+    (order Q, K, V, seeded), each tensor divided by max|x| / 448 and rounded to
+    e4m3 (torch's conversion).  Returns ((q8, k8, v8), (sq, sk, sv)) on the CPU;
+    the real inputs are sq * q8.float(), and so on."""
+    g = torch.Generator().manual_seed(int(seed))
+    shape = (B, H, N, d)
+    xs = [torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(3)]
+    out, scales = [], []
+    for x in xs:
+        s = float(x.abs().max()) / FP8_MAX
+        out.append((x / s).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn))
+        scales.append(s)
+    return tuple(out), tuple(scales)

@@ -143,6 +143,22 @@ attn_status attn_bwd_blocksparse(const void* Q, const void* K, const void* V, co
                                  void* dQ, void* dK, void* dV, attn_dtype grad_dt,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* fp8 forward.  FlashAttention-2 review, research-directions answer: FP8
+ * support is the gap it names for newer hardware.  Q, K, V: device OCP fp8
+ * e4m3 ("e4m3fn": no infinities, max 448) [B,H,N,d] arrays whose real values
+ * are q_descale * Q, k_descale * K, v_descale * V (one factor per tensor, any
+ * finite value).  Computes the same O and LSE as attn_fwd on those real values,
+ * with O in bf16 (RNE) and LSE in fp32.  d must be 64 or 128 (else
+ * ATTN_EUNSUPPORTED).  Arithmetic: Q K^T from fp8 products, exact, summed in
+ * fp32; the probabilities P are rounded to fp8 e4m3 (RNE, relative error at most
+ * 2^-4, or 2^-10 absolute below 2^-6) before the P V product, and the row sum
+ * is taken over exactly those rounded values; the largest P of each row is at
+ * least 2^7.  Other arguments, errors and ownership as for attn_fwd. */
+attn_status attn_fwd_fp8(const void* Q, const void* K, const void* V,
+                         float q_descale, float k_descale, float v_descale,
+                         int B, int H, int N, int d, float scale, int causal,
+                         void* O, float* LSE, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* attn_status_str(attn_status s);
 

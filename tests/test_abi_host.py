@@ -96,6 +96,20 @@ def test_blocksparse_rejects_bad_masks_before_launch():
     assert bwd(heads=6, wsb=ws - 1) == attn.ATTN_EINVAL
 
 
+def test_fp8_rejects_before_launch():
+    L = attn.lib()
+    f = lambda q=P, d=128, sq=1.0, scale=0.1, causal=0: L.attn_fwd_fp8(q, P, P, sq, 1.0, 1.0, 1, 2, 64, d, scale,
+                                                                       causal, P, P, None)
+    assert f(d=80) == attn.ATTN_EUNSUPPORTED          # 64-byte contraction steps: d = 64 or 128
+    assert f(d=96) == attn.ATTN_EUNSUPPORTED
+    assert f(sq=math.nan) == attn.ATTN_EINVAL
+    assert f(sq=math.inf) == attn.ATTN_EINVAL
+    assert f(scale=math.nan) == attn.ATTN_EINVAL
+    assert f(causal=3) == attn.ATTN_EINVAL
+    assert f(q=MIS) == attn.ATTN_EINVAL
+    assert f(q=NUL) == attn.ATTN_EINVAL
+
+
 def test_workspace_sizes():
     L = attn.lib()
     rows = 4 * 16 * 4096
