@@ -25,13 +25,14 @@ sys.path.insert(0, ROOT)
 import torch  # noqa: E402
 
 from exact_tiled_attention_12_amd import (attn_bwd_blocksparse, attn_bwd_dkdv, attn_bwd_dq,  # noqa: E402
-                                          attn_bwd_preprocess, attn_fwd, attn_fwd_blocksparse)
+                                          attn_bwd_preprocess, attn_fwd, attn_fwd_blocksparse, attn_fwd_fp8)
 from exact_tiled_attention_12_amd.configs import CONFIGS  # noqa: E402
 from exact_tiled_attention_12_amd.flops import attn_flops, blocksparse_flops  # noqa: E402
-from exact_tiled_attention_12_amd.inputs import config_inputs, local_global_mask  # noqa: E402
+from exact_tiled_attention_12_amd.inputs import config_inputs, local_global_mask, make_fp8_inputs  # noqa: E402
 
 METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak at N=4k/16k, d=128"
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5033.2           # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 KERNEL_SOURCES = ["exact_tiled_attention_12_amd/csrc/attn_fwd.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_bwd.hip",
@@ -159,6 +160,31 @@ class SparseWorkload:
         return wall, t_fwd, t_bwd
 
 
+def fp8_forward(cfg, dev, steps, warmup):
+    """attn_fwd_fp8 on a workload's shape (fp8 e4m3 Q, K, V with per-tensor factors, O in bf16):
+    mean HIP-event time per launch over `steps` launches on the current stream."""
+    (q8, k8, v8), (sq, sk, sv) = make_fp8_inputs(cfg.B, cfg.H, cfg.N, cfg.d, seed=cfg.seed)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q8.shape[:-1], dtype=torch.float32, device=dev)
+    run = lambda: attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=cfg.causal, out=o, lse=lse)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / steps * 1e-3
+    fl = attn_flops(cfg.B, cfg.H, cfg.N, cfg.d, cfg.causal, "fwd")
+    return {"workload": f"B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} causal={cfg.causal}, fp8 e4m3 Q/K/V "
+                        f"(per-tensor factors), O bf16", "us": round(t * 1e6, 2),
+            "tflops": round(fl / t / 1e12, 2), "frac_fp8_peak": round(fl / t / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "frac_bf16_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_baseline(cfg, budget_s=12.0):
     """The fp64 oracle (as it stands) on whole heads of the same workload, fwd + bwd."""
     import oracle
@@ -202,6 +228,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the N=16k measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward measurement")
+    ap.add_argument("--fp8-only", action="store_true", help="only the fp8 forward (for profiling)")
     ap.add_argument("--sparse-only", action="store_true",
                     help="only the block-sparse measurement (prints its JSON object; for profiling)")
     ap.add_argument("--copy-only", action="store_true",
@@ -224,6 +252,13 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": a.numel(), "launches": 3}))
+        return
+
+    if args.fp8_only:
+        for ci in (3, 4):
+            r = fp8_forward(CONFIGS[ci], dev, args.steps, args.warmup)
+            log(f"bench: fp8 forward {r['workload']}: {r['us']} us, {r['tflops']} TFLOP/s")
+            print(json.dumps(r), flush=True)
         return
 
     if args.sparse_only:
@@ -319,6 +354,13 @@ def main():
             "kept_fraction_of_causal_flops": round((ws.fl_fwd + ws.fl_bwd) / ws.fl_dense, 4),
         }
         log(f"bench: block-sparse step {wall_s * 1e3:.3f} ms; fwd {tf_s * 1e6:.1f} us, bwd {tb_s * 1e6:.1f} us")
+
+    if cfg.index == 3 and not args.no_fp8:
+        torch.cuda.empty_cache()
+        out["fp8_forward"] = [fp8_forward(CONFIGS[ci], dev, max(5, args.steps), max(2, args.warmup // 2))
+                              for ci in (3, 4)]
+        log("bench: fp8 forward " + "; ".join(f"{r['workload'].split(',')[0]}: {r['us']} us, {r['tflops']} TFLOP/s"
+                                               for r in out["fp8_forward"]))
 
     if not args.no_cpu:
         log("bench: CPU oracle baseline")

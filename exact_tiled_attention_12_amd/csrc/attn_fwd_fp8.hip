@@ -39,12 +39,13 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kFp8Headroom = 7.0f;          // log2 distance of a new reference below the row max
 constexpr int kFp8One4 = 0x38383838;          // four e4m3 1.0
+constexpr int kFp8KeyTile = 64;               // keys per tile (64 or 128)
 
 __device__ __forceinline__ int f8_swz(int r) { return ((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4); }
 
-template <int D>
+template <int D, int BN_ = 64>
 struct Fp8Cfg {
-    static constexpr int BM = 128, BN = 64, NKT = 2, RB = 128;
+    static constexpr int BM = 128, BN = BN_, NKT = BN / 32, NPV = BN / 64, RB = 128;
     static constexpr int NS = D / 64;          // 64-byte contraction steps of S
     static constexpr int NDT = D / 32;         // 32-row tiles of O^T
     static constexpr int T_BYTES = BN * RB;
@@ -76,13 +77,13 @@ __device__ __forceinline__ i32x8 cat8(u32x4 a, u32x4 b)
     return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int BN = 64>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                          const uint8_t* __restrict__ V, bf16* __restrict__ O,
                                                          float* __restrict__ LSE, int N, int nqblk, float c,
                                                          float v_scale, int negate_q)
 {
-    using C = Fp8Cfg<D>;
+    using C = Fp8Cfg<D, BN>;
     constexpr float NEG_INF = -__builtin_inff();
     __shared__ __attribute__((aligned(1024))) char sK0[C::T_BYTES], sK1[C::T_BYTES];
     __shared__ __attribute__((aligned(1024))) char sV0[C::T_BYTES], sV1[C::T_BYTES];
@@ -188,29 +189,34 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_fp8(const uint8_t* __restri
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
             mc = mnew;
         }
-        // P in fp8, bytes in (kt, r) order: the B operand of the P V and row-sum products
-        int pw[8];
+        // P in fp8, bytes in (kt, r) order, 64 keys per contraction step: the B operands of
+        // the P V and row-sum products
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            float p[4];
+        for (int ks = 0; ks < C::NPV; ++ks) {
+            int pw[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float sv = sacc[w >> 2][4 * (w & 3) + e];
-                p[e] = need_mask && sv == NEG_INF ? 0.f : fast_exp2(fmaf(sv, c, -mc));
+            for (int w = 0; w < 8; ++w) {
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sv = sacc[2 * ks + (w >> 2)][4 * (w & 3) + e];
+                    p[e] = need_mask && sv == NEG_INF ? 0.f : fast_exp2(fmaf(sv, c, -mc));
+                }
+                int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
             }
-            int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-            pw[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
-        }
-        const i32x8 pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-        lacc = mfma_fp8(ones, pf, lacc);
-        // O^T += V^T P^T: four 8-byte transpose reads per 32-row tile of V^T
+            const i32x8 pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+            lacc = mfma_fp8(ones, pf, lacc);
+            // O^T += V^T P^T: four 8-byte transpose reads per 32-row tile of V^T
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-            i32x2 t[4];
+            for (int dt = 0; dt < C::NDT; ++dt) {
+                i32x2 t[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) t[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sV + vo[dt] + i * 2048));
-            const i32x8 a = {t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
-            oacc[dt] = mfma_fp8(a, pf, oacc[dt]);
+                for (int i = 0; i < 4; ++i)
+                    t[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(sV + ks * 64 * 128 + vo[dt] + i * 2048));
+                const i32x8 a = {t[0][0], t[0][1], t[1][0], t[1][1], t[2][0], t[2][1], t[3][0], t[3][1]};
+                oacc[dt] = mfma_fp8(a, pf, oacc[dt]);
+            }
         }
     };
 
@@ -254,7 +260,7 @@ static hipError_t launch_fp8_dc(const void* Q, const void* K, const void* V, voi
                                 float c, float v_scale, int negq, hipStream_t st)
 {
     const int nqblk = (N + Fp8Cfg<D>::BM - 1) / Fp8Cfg<D>::BM;
-    hipLaunchKernelGGL((fwd_kernel_fp8<D, CAUSAL>), dim3(nqblk * BH), dim3(256), 0, st, (const uint8_t*)Q,
+    hipLaunchKernelGGL((fwd_kernel_fp8<D, CAUSAL, kFp8KeyTile>), dim3(nqblk * BH), dim3(256), 0, st, (const uint8_t*)Q,
                        (const uint8_t*)K, (const uint8_t*)V, (bf16*)O, LSE, N, nqblk, c, v_scale, negq);
     return hipGetLastError();
 }
