@@ -37,7 +37,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
 KERNEL_SOURCES = ["exact_tiled_attention_12_amd/csrc/attn_fwd.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_bwd.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_fwd_fp8.hip",
-                  "exact_tiled_attention_12_amd/csrc/attn_common.h"]
+                  "exact_tiled_attention_12_amd/csrc/attn_common.h",
+                  "exact_tiled_attention_12_amd/csrc/attn_tuning.h"]
 
 
 def source_hash():

@@ -35,6 +35,15 @@ class AttnError(RuntimeError):
         super().__init__(f"{where}: {msg}")
 
 
+def use_library(path):
+    """Loads the library from `path` instead of the in-tree libattn.so (before the first call;
+    the launch-parameter sweep times candidate builds this way)."""
+    global LIB_PATH
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(LIB_PATH):
+        raise RuntimeError("the library is already loaded")
+    LIB_PATH = path
+
+
 def lib():
     """Loads libattn.so (raises if it has not been built)."""
     global _lib

@@ -17,8 +17,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose=False, extra=()):
-    tmp = LIB_PATH + ".tmp"
+def build(verbose=False, extra=(), out=None):
+    """Compiles libattn.so (or, with `out`, a library at that path; `extra` adds hipcc flags)."""
+    target = out or LIB_PATH
+    tmp = target + ".tmp"
     cmd = [HIPCC, *FLAGS, *extra, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -29,8 +31,8 @@ def build(verbose=False, extra=()):
         raise RuntimeError("hipcc failed:\n" + errs)
     if errs.strip() and verbose:
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

@@ -28,6 +28,7 @@
 // waves whose keys all follow a block's queries get P = 0 (or skip the block).
 #include "attn_common.h"
 #include "attn_launch.h"
+#include "attn_tuning.h"
 
 namespace attn {
 
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_kernel_f32(const float* __restrict__ 
                                                       const float* __restrict__ Dg,
                                                       float* __restrict__ dQacc, float* __restrict__ dK,
                                                       float* __restrict__ dV, int N, int nkblk, float scale,
-                                                      const uint8_t* __restrict__ bmask, long mhead)
+                                                      const uint8_t* __restrict__ bmask, long mhead, int slots)
 {
     typedef float T;
     using C = BwdCfg<T, D>;
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) void bwd_kernel_f32(const float* __restrict__ 
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, kb;
-    block_coords<CAUSAL, false, 32>(blockIdx.x, gridDim.x, nkblk, head, kb);
+    block_coords<CAUSAL, false>(blockIdx.x, gridDim.x, nkblk, slots, head, kb);
     const int k0 = kb * C::BN;
     const int k0w = k0 + 32 * wave;            // this wave's first key
     const int mykey = k0w + l32;
@@ -412,7 +413,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                                                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE, const float* __restrict__ Dg,
                                                      G* __restrict__ dK, G* __restrict__ dV, int N, int nkblk,
-                                                     float scale, const uint8_t* __restrict__ bmask, long mhead)
+                                                     float scale, const uint8_t* __restrict__ bmask, long mhead,
+                                                     int slots)
 {
     using C = BwdKVCfg<D>;
     static_assert(kMaskBlock == C::BN && kMaskBlock == 2 * C::BM, "mask block = key block");
@@ -429,7 +431,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, kb;
-    block_coords<CAUSAL, false, 32>(blockIdx.x, gridDim.x, nkblk, head, kb);
+    block_coords<CAUSAL, false>(blockIdx.x, gridDim.x, nkblk, slots, head, kb);
     const int k0 = kb * C::BN;
     const int k0w = k0 + 32 * kg;
     const int mykey = k0w + l32;
@@ -664,7 +666,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
                                                       const bf16* __restrict__ V, const bf16* __restrict__ dO,
                                                       const float* __restrict__ LSE, const float* __restrict__ Dg,
                                                       G* __restrict__ dQ, int N, int nqblk, float scale,
-                                                      const uint8_t* __restrict__ bmask, long mhead)
+                                                      const uint8_t* __restrict__ bmask, long mhead, int slots)
 {
     using C = BwdQCfg<D>;
     static_assert(kMaskBlock == C::BM && kMaskBlock == 2 * C::BN, "mask block = query block");
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, qb;
-    block_coords<CAUSAL, true, 64>(blockIdx.x, gridDim.x, nqblk, head, qb);
+    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, slots, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + 32 * wave;
     const int myq = q0w + l32;
@@ -871,12 +873,15 @@ static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void
 {
     const int nkblk = (N + BwdKVCfg<D>::BN - 1) / BwdKVCfg<D>::BN;
     const dim3 grid(nkblk * BH), block(64 * BwdKVCfg<D>::WAVES);
+    const int slots = tune_lookup(kTuneDkdv, D, CAUSAL, N).slots;
     if (bmask)
         hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G, true>), grid, block, 0, st, (const bf16*)Q, (const bf16*)K,
-                           (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, bmask, mhead);
+                           (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, bmask, mhead,
+                           slots);
     else
         hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G, false>), grid, block, 0, st, (const bf16*)Q, (const bf16*)K,
-                           (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, nullptr, 0L);
+                           (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, nullptr, 0L,
+                           slots);
     return hipGetLastError();
 }
 
@@ -886,14 +891,15 @@ static hipError_t dq_t(const void* Q, const void* K, const void* V, const void* 
                        hipStream_t st)
 {
     const int nqblk = (N + BwdQCfg<D>::BM - 1) / BwdQCfg<D>::BM;
+    const int slots = tune_lookup(kTuneDq, D, CAUSAL, N).slots;
     if (bmask)
         hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G, true>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
                            (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale, bmask,
-                           mhead);
+                           mhead, slots);
     else
         hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G, false>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
                            (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale,
-                           nullptr, 0L);
+                           nullptr, 0L, slots);
     return hipGetLastError();
 }
 
@@ -934,14 +940,15 @@ static hipError_t f32_t(const void* Q, const void* K, const void* V, const void*
     const long n4 = (long)BH * N * D / 4;
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dQacc, n4);
     const int nkblk = (N + C::BN - 1) / C::BN;
+    const int slots = tune_lookup(kTuneBwdF32, D, CAUSAL, N).slots;
     if (bmask)
         hipLaunchKernelGGL((bwd_kernel_f32<D, CAUSAL, true>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
                            (const float*)Q, (const float*)K, (const float*)V, (const float*)dO, LSE, Dd, dQacc, dK,
-                           dV, N, nkblk, scale, bmask, mhead);
+                           dV, N, nkblk, scale, bmask, mhead, slots);
     else
         hipLaunchKernelGGL((bwd_kernel_f32<D, CAUSAL, false>), dim3(nkblk * BH), dim3(C::THREADS), 0, st,
                            (const float*)Q, (const float*)K, (const float*)V, (const float*)dO, LSE, Dd, dQacc, dK,
-                           dV, N, nkblk, scale, nullptr, 0L);
+                           dV, N, nkblk, scale, nullptr, 0L, slots);
     return hipGetLastError();
 }
 

@@ -290,12 +290,13 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 // Each XCD works through its own heads in groups of G, a group's blocks
 // longest-first (the heaviest block of every head in the group before any lighter
 // one), the next group's heavy blocks filling the slots its light blocks free.
-// G is the smallest head count whose blocks fill the XCD's SLOTS workgroup slots,
+// G is the smallest head count whose blocks fill the XCD's `slots` workgroup slots,
 // so the tail stays short while the K/V of only G heads compete for the XCD's L2.
 // HEAVY_LAST: a head's last block costs most (query-side kernels); otherwise its
 // first (key-side kernels).  Without 8 | BH the whole GPU is one group sequence.
-template <bool CAUSAL, bool HEAVY_LAST, int SLOTS>
-__device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int& head, int& blk)
+// (`slots` comes from the launch-parameter table of attn_tuning.h.)
+template <bool CAUSAL, bool HEAVY_LAST>
+__device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int SLOTS, int& head, int& blk)
 {
     if constexpr (!CAUSAL) {
         const int b = xcd_remap(bid, nb);

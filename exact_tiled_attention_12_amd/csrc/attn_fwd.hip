@@ -29,6 +29,7 @@
 #include "../../include/attn.h"
 #include "attn_common.h"
 #include "attn_launch.h"
+#include "attn_tuning.h"
 
 static_assert(ATTN_MASK_BLOCK == attn::kMaskBlock, "the ABI's mask block is the kernels'");
 
@@ -65,7 +66,8 @@ template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) void fwd_kernel_f32(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int N, int nqblk, float c,
-                                                      int negate_q, const uint8_t* __restrict__ bmask, long mhead)
+                                                      int negate_q, const uint8_t* __restrict__ bmask, long mhead,
+                                                      int slots)
 {
     typedef float T;
     using C = FwdCfg<T, D>;
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(const float* __restrict__ 
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, qb;
-    block_coords<CAUSAL, true, 32>(blockIdx.x, gridDim.x, nqblk, head, qb);
+    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, slots, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + wave * 32 * QT;             // this wave's first query row
     const size_t hoff = (size_t)head * (size_t)N * D;
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
                                                           const bf16* __restrict__ V, bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int N, int nqblk, float c,
                                                           int negate_q, const uint8_t* __restrict__ bmask,
-                                                          long mhead)
+                                                          long mhead, int slots)
 {
     static_assert(kMaskBlock == 2 * FwdBf16Cfg<D>::BN && kMaskBlock == FwdBf16Cfg<D>::BM, "mask block = query block");
     using C = FwdBf16Cfg<D>;
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, qb;
-    block_coords<CAUSAL, true, 64>(blockIdx.x, gridDim.x, nqblk, head, qb);
+    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, slots, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + 32 * wave;
     const int myq = q0w + l32;
@@ -589,9 +591,10 @@ static hipError_t launch_fwd_f32(const void* Q, const void* K, const void* V, vo
     const int nqblk = (N + C::BM - 1) / C::BM;
     const float c = fabsf(scale) * kLog2e;
     const int negq = scale < 0.f;
+    const int slots = tune_lookup(kTuneFwdF32, D, CAUSAL, N).slots;
     hipLaunchKernelGGL((fwd_kernel_f32<D, CAUSAL, SPARSE>), dim3(nqblk * BH), dim3(C::THREADS), 0, st,
                        (const float*)Q, (const float*)K, (const float*)V, (float*)O, LSE, N, nqblk, c, negq, bmask,
-                       mhead);
+                       mhead, slots);
     return hipGetLastError();
 }
 
@@ -602,7 +605,7 @@ static hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, v
     const int nqblk = (N + FwdBf16Cfg<D>::BM - 1) / FwdBf16Cfg<D>::BM;
     hipLaunchKernelGGL((fwd_kernel_bf16<D, CAUSAL, SPARSE>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
                        (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk, fabsf(scale) * kLog2e,
-                       (int)(scale < 0.f), bmask, mhead);
+                       (int)(scale < 0.f), bmask, mhead, tune_lookup(kTuneFwdBf16, D, CAUSAL, N).slots);
     return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@
 #include "../../include/attn.h"
 #include "attn_common.h"
 #include "attn_launch.h"
+#include "attn_tuning.h"
 
 namespace attn {
 
@@ -39,7 +40,6 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr float kFp8Headroom = 7.0f;          // log2 distance of a new reference below the row max
 constexpr int kFp8One4 = 0x38383838;          // four e4m3 1.0
-constexpr int kFp8KeyTile = 64;               // keys per tile (64 or 128)
 
 __device__ __forceinline__ int f8_swz(int r) { return ((r >> 2) & 1) | (r & 2) | ((r >> 1) & 4); }
 
@@ -81,7 +81,7 @@ template <int D, bool CAUSAL, int BN = 64>
 __global__ __launch_bounds__(256, 2) void fwd_kernel_fp8(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                          const uint8_t* __restrict__ V, bf16* __restrict__ O,
                                                          float* __restrict__ LSE, int N, int nqblk, float c,
-                                                         float v_scale, int negate_q)
+                                                         float v_scale, int negate_q, int slots)
 {
     using C = Fp8Cfg<D, BN>;
     constexpr float NEG_INF = -__builtin_inff();
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_fp8(const uint8_t* __restri
     const int l32 = lane & 31, h = lane >> 5;
 
     int head, qb;
-    block_coords<CAUSAL, true, 64>(blockIdx.x, gridDim.x, nqblk, head, qb);
+    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, slots, head, qb);
     const int q0 = qb * C::BM;
     const int q0w = q0 + 32 * wave;
     const int myq = q0w + l32;
@@ -260,8 +260,13 @@ static hipError_t launch_fp8_dc(const void* Q, const void* K, const void* V, voi
                                 float c, float v_scale, int negq, hipStream_t st)
 {
     const int nqblk = (N + Fp8Cfg<D>::BM - 1) / Fp8Cfg<D>::BM;
-    hipLaunchKernelGGL((fwd_kernel_fp8<D, CAUSAL, kFp8KeyTile>), dim3(nqblk * BH), dim3(256), 0, st, (const uint8_t*)Q,
-                       (const uint8_t*)K, (const uint8_t*)V, (bf16*)O, LSE, N, nqblk, c, v_scale, negq);
+    const TuneEntry t = tune_lookup(kTuneFwdFp8, D, CAUSAL, N);
+    if (t.key_tile == 128)
+        hipLaunchKernelGGL((fwd_kernel_fp8<D, CAUSAL, 128>), dim3(nqblk * BH), dim3(256), 0, st, (const uint8_t*)Q,
+                           (const uint8_t*)K, (const uint8_t*)V, (bf16*)O, LSE, N, nqblk, c, v_scale, negq, t.slots);
+    else
+        hipLaunchKernelGGL((fwd_kernel_fp8<D, CAUSAL, 64>), dim3(nqblk * BH), dim3(256), 0, st, (const uint8_t*)Q,
+                           (const uint8_t*)K, (const uint8_t*)V, (bf16*)O, LSE, N, nqblk, c, v_scale, negq, t.slots);
     return hipGetLastError();
 }
 

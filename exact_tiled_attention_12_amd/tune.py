@@ -1,0 +1,234 @@
+"""Offline sweep of the launch parameters in csrc/attn_tuning.h (run on an MI355X).
+
+FlashAttention-2 review, implementation-cost answer, section 1 (2) and the
+auto-tuning answer: the block configuration is tuned per GPU ahead of time and
+looked up at launch.  Candidates are whole builds of the library with the table
+overridden (ATTN_TUNE_FORCE_SLOTS, ATTN_TUNE_FORCE_KEY_TILE); each is timed in a
+process of its own on the workload shapes, and the fastest per (kernel, head dim,
+causal, N) goes into the table.
+
+    python -m exact_tiled_attention_12_amd.tune build --out DIR     # candidate builds (CPU is enough)
+    python -m exact_tiled_attention_12_amd.tune time --lib PATH     # one candidate (GPU), JSON lines
+    python -m exact_tiled_attention_12_amd.tune sweep --libs DIR --results FILE   # time every candidate (GPU)
+    python -m exact_tiled_attention_12_amd.tune apply --results FILE  # write the table and profiles/tuning_sweep.md
+"""
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import re
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+TABLE_H = os.path.join(HERE, "csrc", "attn_tuning.h")
+REPORT = os.path.join(ROOT, "profiles", "tuning_sweep.md")
+
+SLOTS = (16, 32, 64, 128)
+KEY_TILES = (64, 128)
+
+# (table kernel name, case label, dtype, B, H, N, d, causal): the workload shapes whose launches depend
+# on the swept parameters (the causal schedule; the fp8 key tile also without a mask)
+CASES = [
+    ("kTuneFwdBf16", "fwd bf16", "bf16", 4, 16, 4096, 128, True),
+    ("kTuneFwdBf16", "fwd bf16", "bf16", 1, 16, 16384, 128, True),
+    ("kTuneFwdBf16", "fwd bf16", "bf16", 8, 32, 2048, 80, True),
+    ("kTuneDkdv", "dK/dV", "bf16", 4, 16, 4096, 128, True),
+    ("kTuneDkdv", "dK/dV", "bf16", 1, 16, 16384, 128, True),
+    ("kTuneDkdv", "dK/dV", "bf16", 8, 32, 2048, 80, True),
+    ("kTuneDq", "dQ", "bf16", 4, 16, 4096, 128, True),
+    ("kTuneDq", "dQ", "bf16", 1, 16, 16384, 128, True),
+    ("kTuneDq", "dQ", "bf16", 8, 32, 2048, 80, True),
+    ("kTuneFwdFp8", "fwd fp8", "fp8", 4, 16, 4096, 128, True),
+    ("kTuneFwdFp8", "fwd fp8", "fp8", 1, 16, 16384, 128, True),
+    ("kTuneFwdFp8", "fwd fp8", "fp8", 4, 16, 4096, 128, False),
+    ("kTuneFwdFp8", "fwd fp8", "fp8", 8, 16, 1024, 64, False),
+]
+# the kernels the table also holds but the sweep leaves at their defaults
+FIXED = [("kTuneFwdF32", 0, 1, 32, 64), ("kTuneBwdF32", 0, 1, 32, 64)]
+DEFAULT = {"kTuneFwdBf16": (64, 64), "kTuneDkdv": (32, 64), "kTuneDq": (64, 64), "kTuneFwdFp8": (64, 64)}
+HYSTERESIS = 1.01       # a candidate replaces the default only if it is more than 1% faster
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lib_name(slots, key_tile):
+    return f"libattn_s{slots}_k{key_tile}.so"
+
+
+def candidates():
+    return [(s, k) for s in SLOTS for k in KEY_TILES]
+
+
+def build_all(out_dir, jobs=4):
+    from .build import build
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(sk):
+        s, k = sk
+        path = os.path.join(out_dir, lib_name(s, k))
+        build(extra=[f"-DATTN_TUNE_FORCE_SLOTS={s}", f"-DATTN_TUNE_FORCE_KEY_TILE={k}"], out=path)
+        _say(f"tune: built {path}")
+        return path
+
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        return list(ex.map(one, candidates()))
+
+
+def time_cases(lib_path, reps=20, warmup=5):
+    """Times every case with the given library (this process loads no other)."""
+    import torch
+    from . import attn
+    attn.use_library(lib_path)
+    from .inputs import make_fp8_inputs, make_inputs
+    dev = torch.device("cuda:0")
+    out = []
+    for kern, label, dtype, B, H, N, d, causal in CASES:
+        if dtype == "fp8":
+            (q8, k8, v8), (sq, sk, sv) = make_fp8_inputs(B, H, N, d, seed=1)
+            q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+            run = lambda: attn.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal)
+        else:
+            q, k, v, do = (t.to(dev) for t in make_inputs(B, H, N, d, dtype, seed=1))
+            o, lse = attn.attn_fwd(q, k, v, causal=causal)
+            D = attn.attn_bwd_preprocess(o, do)
+            if kern == "kTuneFwdBf16":
+                run = lambda: attn.attn_fwd(q, k, v, causal=causal, out=o, lse=lse)
+            elif kern == "kTuneDkdv":
+                dk, dv = torch.empty(q.shape, device=dev), torch.empty(q.shape, device=dev)
+                run = lambda: attn.attn_bwd_dkdv(q, k, v, do, lse, D, causal=causal, dk=dk, dv=dv)
+            else:
+                dq = torch.empty(q.shape, device=dev)
+                run = lambda: attn.attn_bwd_dq(q, k, v, do, lse, D, causal=causal, dq=dq)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        out.append({"kernel": kern, "label": label, "B": B, "H": H, "N": N, "d": d, "causal": causal, "us": us})
+        _say(f"tune: {os.path.basename(lib_path)} {label} B{B} H{H} N{N} d{d} causal={causal}: {us:.1f} us")
+        torch.cuda.empty_cache()
+    return out
+
+
+def _table(best):
+    """best: {(kernel, d, causal, N): (slots, key_tile)} -> C++ table rows."""
+    rows = []
+    groups = {}
+    for (kern, d, causal, N), v in best.items():
+        groups.setdefault((kern, d, causal), []).append((N, v))
+    for (kern, d, causal), lst in sorted(groups.items()):
+        lst.sort()
+        for i, (N, (s, k)) in enumerate(lst):
+            n_max = N if i + 1 < len(lst) else "1 << 30"
+            rows.append(f"    {{{kern}, {d}, {int(causal)}, {n_max}, {s}, {k}}},")
+    for kern, (s, k) in DEFAULT.items():                   # every other shape: the previous defaults
+        rows.append(f"    {{{kern}, 0, 1, 1 << 30, {s}, {k}}},")
+        if kern == "kTuneFwdFp8":
+            rows.append(f"    {{{kern}, 0, 0, 1 << 30, {s}, {k}}},")
+    for kern, d, causal, s, k in FIXED:
+        rows.append(f"    {{{kern}, {d}, {causal}, 1 << 30, {s}, {k}}},")
+    return rows
+
+
+def sweep(lib_dir, reps, results_path):
+    results = {}
+    for s, k in candidates():
+        path = os.path.join(lib_dir, lib_name(s, k))
+        t0 = time.time()
+        r = subprocess.run([sys.executable, "-m", "exact_tiled_attention_12_amd.tune", "time", "--lib", path,
+                            "--reps", str(reps)], cwd=ROOT, capture_output=True, text=True, timeout=600)
+        sys.stderr.write(r.stderr)
+        if r.returncode != 0:
+            raise RuntimeError(f"timing {path} failed ({r.returncode})")
+        results[(s, k)] = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+        _say(f"tune: candidate slots={s} key_tile={k} done in {time.time() - t0:.0f} s")
+    with open(results_path, "w") as f:
+        json.dump({"reps": reps, "candidates": [{"slots": s, "key_tile": k, "cases": results[(s, k)]}
+                                                for (s, k) in candidates()]}, f, indent=1)
+    _say(f"tune: wrote {results_path}")
+
+
+def apply(results_path, table_path=TABLE_H, report_path=REPORT):
+    with open(results_path) as f:
+        data = json.load(f)
+    reps = data["reps"]
+    results = {(c["slots"], c["key_tile"]): c["cases"] for c in data["candidates"]}
+    # choose: slots for the bf16 kernels (their key tile is fixed: read the k = 64 builds),
+    # (slots, key tile) for the fp8 forward
+    best, report = {}, []
+    for ci, (kern, label, dtype, B, H, N, d, causal) in enumerate(CASES):
+        # the bf16 kernels have a fixed key tile (read the k = 64 builds); without a mask the
+        # schedule ignores `slots` (read the default's builds)
+        opts = [(s, k) for (s, k) in candidates() if (kern == "kTuneFwdFp8" or k == 64)
+                and (causal or s == DEFAULT[kern][0])]
+        times = {sk: results[sk][ci]["us"] for sk in opts}
+        default = DEFAULT[kern]
+        choice = min(times, key=times.get)
+        if default in times and times[default] <= HYSTERESIS * times[choice]:
+            choice = default                      # within run-to-run noise of the best: keep the default
+        best[(kern, d, causal, N)] = choice
+        report.append((label, B, H, N, d, causal, times, choice, default))
+    # table
+    with open(table_path) as f:
+        text = f.read()
+    rows = "\n".join(_table(best))
+    text = re.sub(r"(// ---- generated table: begin ----\nstatic constexpr TuneEntry kTuneTable\[\] = \{\n)(.*?)(\n\};\n// ---- generated table: end ----)",
+                  lambda m: m.group(1) + rows + m.group(3), text, flags=re.S)
+    with open(table_path, "w") as f:
+        f.write(text)
+    # report
+    md = ["# Launch-parameter sweep (csrc/attn_tuning.h)", "",
+          "Command (from the repository root on the GPU box; the candidate libraries built first with "
+          "`python -m exact_tiled_attention_12_amd.tune build --out DIR`):", "", "```",
+          f"python -m exact_tiled_attention_12_amd.tune sweep --libs DIR --reps {reps} --results FILE",
+          "python -m exact_tiled_attention_12_amd.tune apply --results FILE", "```", "", "The raw timings are in `profiles/tuning_sweep_results.json`.", "",
+          "Mean HIP-event time per launch (µs) of each candidate; `slots` is the causal schedule's L2 group size, "
+          "`kt` the fp8 key tile.  Each candidate library is timed in a process of its own.  A candidate "
+          "replaces the default only when it is more than 1% faster (run-to-run noise is about that size).", ""]
+    for label, B, H, N, d, causal, times, choice, default in report:
+        head = " | ".join(f"s{s}" + (f"/kt{k}" if label == "fwd fp8" else "") for (s, k) in times)
+        md.append(f"**{label}, B{B} H{H} N{N} d{d} causal={causal}**: chosen slots {choice[0]}"
+                  + (f", key tile {choice[1]}" if label == "fwd fp8" else "")
+                  + f" ({times[choice]:.1f} µs; previous default {times.get(default, float('nan')):.1f} µs)")
+        md.append("")
+        md.append(f"| {head} |")
+        md.append("|" + "---|" * len(times))
+        md.append("| " + " | ".join(f"{t:.1f}" for t in times.values()) + " |")
+        md.append("")
+    with open(report_path, "w") as f:
+        f.write("\n".join(md) + "\n")
+    _say(f"tune: wrote {table_path} and {report_path}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("mode", choices=["build", "time", "sweep", "apply"])
+    ap.add_argument("--out", default="tune_libs")
+    ap.add_argument("--lib")
+    ap.add_argument("--libs")
+    ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--results", default="tune_results.json")
+    a = ap.parse_args()
+    if a.mode == "build":
+        build_all(a.out)
+    elif a.mode == "time":
+        for r in time_cases(a.lib, reps=a.reps):
+            print(json.dumps(r), flush=True)
+    elif a.mode == "sweep":
+        sweep(a.libs, a.reps, a.results)
+    else:
+        apply(a.results)
+
+
+if __name__ == "__main__":
+    main()
