@@ -184,3 +184,24 @@ def test_workload_4_sampled():
         _say(f"  head {hh}:", {n: f"{e:.2e}" for n, e in errs.items()})
         for n, e in errs.items():
             assert e <= TOL["bf16"], f"head {hh} {n}: {e}"
+
+
+def test_long_sequence_sampled():
+    """N = 65536 (four times the longest workload): sampled query rows (O, LSE, dQ) of both
+    heads and key rows (dK, dV) of one, each evaluated by the oracle from its definition."""
+    N = 65536
+    _say(f"case long sequence N={N}")
+    q, k, v, do = make_inputs(1, 2, N, 128, "bf16", seed=65)
+    o, lse, (dq, dk, dv) = _run(q, k, v, do, True)
+    rng = np.random.default_rng(65)
+    rows = np.unique(np.concatenate([[0, 1, 4095, 4096, 32767, N - 1], rng.integers(0, N, 10)]))
+    for hh in (0, 1):
+        Or, Lr, dQr = oracle.rows(q[0, hh], k[0, hh], v[0, hh], do[0, hh], rows, causal=True)
+        ridx = torch.as_tensor(rows)
+        errs = {"O": _err(o[0, hh][ridx], Or), "LSE": _err(lse[0, hh][ridx], Lr), "dQ": _err(dq[0, hh][ridx], dQr)}
+        if hh == 1:          # key rows need every query's statistics: O(N^2 d) on the CPU, one head
+            dKc, dVc = oracle.cols(q[0, hh], k[0, hh], v[0, hh], do[0, hh], rows, causal=True)
+            errs.update(dK=_err(dk[0, hh][ridx], dKc), dV=_err(dv[0, hh][ridx], dVc))
+        _say(f"  head {hh}:", {n: f"{e:.2e}" for n, e in errs.items()})
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], f"head {hh} {n}: {e}"
