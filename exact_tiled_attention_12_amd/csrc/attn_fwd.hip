@@ -510,15 +510,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel_bf16(const bf16* __restrict
                 for (int x = 0; x < 4; ++x) ls[s2] = sum2_bf16(w[x], ls[s2]);
             }
         l += ls[0] + ls[1];
-        // O^T += V^T P^T
+        // O^T += V^T P^T; the V^T fragments (transpose reads) go PF products ahead through a ring
+        {
+            constexpr int NT = 2 * C::NKT * C::NDT, PF = 4;
+            auto tfrag = [&](int t) __attribute__((always_inline)) {
+                return tl.tr(sV, 32 * (t / (2 * C::NDT)) + 16 * ((t / C::NDT) & 1), t % C::NDT);
+            };
+            bf16x8 ring[PF];
 #pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt)
+            for (int t = 0; t < PF; ++t) ring[t] = tfrag(t);
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt)
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sV, 32 * kt + 16 * s2, dt), pf[kt][s2],
-                                                                       oacc[dt], 0, 0, 0);
+            for (int t = 0; t < NT; ++t) {
+                const bf16x8 a = ring[t % PF];
+                if (t + PF < NT) ring[t % PF] = tfrag(t + PF);
+                const int kt = t / (2 * C::NDT), s2 = (t / C::NDT) & 1, dt = t % C::NDT;
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][s2], oacc[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     };
 
     if constexpr (!SPARSE) {
