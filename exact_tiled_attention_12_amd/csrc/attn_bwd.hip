@@ -575,68 +575,81 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         }
     }
 
-    // sum the two query halves' partials: waves 4..7 park theirs in LDS (dK in the
-    // Q/dO buffers, dV in the K/V tiles; lane-contiguous float4s), waves 0..3 add
+    // Epilogue.  The two query halves' partials are summed in LDS, row-major (one key per
+    // row, DP floats, 16-byte chunks XOR-swizzled by the row so that the MFMA-layout writes
+    // and the row reads are free of bank conflicts): dK rows of key group g in the g-th
+    // Q/dO buffer, dV rows in the K/V tiles.  Then all eight waves store whole rows, so
+    // each store instruction writes contiguous memory.
     wait_vmem_all();
     __syncthreads();                                    // every tile fully read
     {
-        char* dkbuf = kg == 0 ? sQ0 : kg == 1 ? sQ1 : kg == 2 ? sG0 : sG1;
-        char* dvbuf = (kg < 2 ? sK : sV) + (kg & 1) * (C::NDT * 16 * 64 * 4);
-        if (qh == 1) {
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int o = ((dt * 4 + g4) * 64 + lane) * 16;
-                    *reinterpret_cast<f32x4*>(dkbuf + o) =
-                        f32x4{dkacc[dt][4 * g4], dkacc[dt][4 * g4 + 1], dkacc[dt][4 * g4 + 2], dkacc[dt][4 * g4 + 3]};
-                    *reinterpret_cast<f32x4*>(dvbuf + o) =
-                        f32x4{dvacc[dt][4 * g4], dvacc[dt][4 * g4 + 1], dvacc[dt][4 * g4 + 2], dvacc[dt][4 * g4 + 3]};
-                }
-        }
-        __syncthreads();
+        constexpr int NCHP = C::DP / 4 <= 16 ? 16 : 32;  // 16-byte chunks per LDS row (power of two)
+        constexpr int GROUP_BYTES = 32 * NCHP * 16;      // one key group's rows
+        static_assert(GROUP_BYTES <= C::Q_BYTES && 2 * GROUP_BYTES <= C::K_BYTES, "epilogue staging fits");
+        auto kbuf = [&](int g) -> char* { return g == 0 ? sQ0 : g == 1 ? sQ1 : g == 2 ? sG0 : sG1; };
+        auto vbuf = [&](int g) -> char* { return (g < 2 ? sK : sV) + (g & 1) * GROUP_BYTES; };
+        auto soff = [](int row, int ch) { return (row * NCHP + (ch ^ (row & 15))) * 16; };
+        char* kb = kbuf(kg);
+        char* vb = vbuf(kg);
+        // lane: key row l32 of the group; accumulator rows d = 32 dt + 8 g4 + 4 h + e -> chunk 8 dt + 2 g4 + h
         if (qh == 0) {
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int o = ((dt * 4 + g4) * 64 + lane) * 16;
-                    const f32x4 pk = *reinterpret_cast<const f32x4*>(dkbuf + o);
-                    const f32x4 pv = *reinterpret_cast<const f32x4*>(dvbuf + o);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        dkacc[dt][4 * g4 + e] += pk[e];
-                        dvacc[dt][4 * g4 + e] += pv[e];
-                    }
+                    const int o = soff(l32, 8 * dt + 2 * g4 + h);
+                    *reinterpret_cast<f32x4*>(kb + o) =
+                        f32x4{dkacc[dt][4 * g4], dkacc[dt][4 * g4 + 1], dkacc[dt][4 * g4 + 2], dkacc[dt][4 * g4 + 3]};
+                    *reinterpret_cast<f32x4*>(vb + o) =
+                        f32x4{dvacc[dt][4 * g4], dvacc[dt][4 * g4 + 1], dvacc[dt][4 * g4 + 2], dvacc[dt][4 * g4 + 3]};
                 }
         }
-    }
-
-    // dK = scale * dK^T acc, dV = dV^T acc, written once (waves 0..3)
-    if (qh == 0 && mykey < N) {
+        __syncthreads();
+        if (qh == 1) {
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt)
+            for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d0 = 32 * dt + 8 * g4 + 4 * h;
-                if (d0 < D) {
-                    G* pk = dK + hoff + (size_t)mykey * D + d0;
-                    G* pv = dV + hoff + (size_t)mykey * D + d0;
-                    if constexpr (sizeof(G) == 4) {
-                        f32x4 a, bb;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int o = soff(l32, 8 * dt + 2 * g4 + h);
+                    f32x4 pk = *reinterpret_cast<const f32x4*>(kb + o);
+                    f32x4 pv = *reinterpret_cast<const f32x4*>(vb + o);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) { a[e] = dkacc[dt][4 * g4 + e] * scale; bb[e] = dvacc[dt][4 * g4 + e]; }
-                        *reinterpret_cast<f32x4*>(pk) = a;
-                        *reinterpret_cast<f32x4*>(pv) = bb;
-                    } else {
-                        bf16x4 a, bb;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) { a[e] = to_bf16(dkacc[dt][4 * g4 + e] * scale); bb[e] = to_bf16(dvacc[dt][4 * g4 + e]); }
-                        *reinterpret_cast<bf16x4*>(pk) = a;
-                        *reinterpret_cast<bf16x4*>(pv) = bb;
+                    for (int e = 0; e < 4; ++e) {
+                        pk[e] += dkacc[dt][4 * g4 + e];
+                        pv[e] += dvacc[dt][4 * g4 + e];
                     }
+                    *reinterpret_cast<f32x4*>(kb + o) = pk;
+                    *reinterpret_cast<f32x4*>(vb + o) = pv;
+                }
+        }
+        __syncthreads();
+        // dK = scale * (dK^T acc)^T, dV = (dV^T acc)^T: D/4 chunks per key row, consecutive threads
+        // take consecutive chunks of a row
+        constexpr int CPR = D / 4, TOTAL = C::BN * CPR, THREADS = 64 * C::WAVES;
+        static_assert(TOTAL % THREADS == 0, "whole passes");
+#pragma unroll
+        for (int pass = 0; pass < TOTAL / THREADS; ++pass) {
+            const int c = pass * THREADS + tid;
+            const int row = c / CPR, ch = c - row * CPR;
+            const int key = k0 + row;
+            const int o = soff(row & 31, ch);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(kbuf(row >> 5) + o);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(vbuf(row >> 5) + o);
+            if (key < N) {
+                G* pk = dK + hoff + (size_t)key * D + 4 * ch;
+                G* pv = dV + hoff + (size_t)key * D + 4 * ch;
+                if constexpr (sizeof(G) == 4) {
+                    *reinterpret_cast<f32x4*>(pk) = a * scale;
+                    *reinterpret_cast<f32x4*>(pv) = b;
+                } else {
+                    bf16x4 x, y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { x[e] = to_bf16(a[e] * scale); y[e] = to_bf16(b[e]); }
+                    *reinterpret_cast<bf16x4*>(pk) = x;
+                    *reinterpret_cast<bf16x4*>(pv) = y;
                 }
             }
+        }
     }
 }
 
