@@ -414,7 +414,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                                                      const float* __restrict__ LSE, const float* __restrict__ Dg,
                                                      G* __restrict__ dK, G* __restrict__ dV, int N, int nkblk,
                                                      float scale, const uint8_t* __restrict__ bmask, long mhead,
-                                                     int slots)
+                                                     int slots, int nitems)
 {
     using C = BwdKVCfg<D>;
     static_assert(kMaskBlock == C::BN && kMaskBlock == 2 * C::BM, "mask block = key block");
@@ -430,8 +430,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     const int kg = wave & 3, qh = wave >> 2;            // key group, query half
     const int l32 = lane & 31, h = lane >> 5;
 
+    // Persistent grid (one workgroup per CU): each workgroup walks its share of the
+    // nitems (head, key block) items, taken in the order block_coords gives an XCD.
+    // Workgroup c of an XCD (of P there) takes positions c, 2P-1-c, 2P+c, 4P-1-c, ...
+    // of that XCD's sequence, so a heavy causal item pairs with a light one.
+    const bool split = CAUSAL ? ((nitems / nkblk) & 7) == 0 : (nitems & 7) == 0;
+    const int xcd = split ? (int)(blockIdx.x & 7) : 0;
+    const int pc = split ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+    const int P = split ? (int)(gridDim.x >> 3) : (int)gridDim.x;
+    const int KX = split ? nitems >> 3 : nitems;
+    for (int t = 0;; ++t) {
+    const int pos = (t & 1) ? (t + 1) * P - 1 - pc : t * P + pc;
+    if (pos >= KX) break;
     int head, kb;
-    block_coords<CAUSAL, false>(blockIdx.x, gridDim.x, nkblk, slots, head, kb);
+    block_coords<CAUSAL, false>(split ? 8 * pos + xcd : pos, nitems, nkblk, slots, head, kb);
     const int k0 = kb * C::BN;
     const int k0w = k0 + 32 * kg;
     const int mykey = k0w + l32;
@@ -591,13 +603,18 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         auto soff = [](int row, int ch) { return (row * NCHP + (ch ^ (row & 15))) * 16; };
         char* kb = kbuf(kg);
         char* vb = vbuf(kg);
+        // lane index made opaque here, so that the offsets below are computed per item and
+        // not hoisted out of the item loop (where they would sit in registers the main loop needs)
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int l32e = lane_e & 31, he = lane_e >> 5, tid_e = 64 * wave + lane_e;
         // lane: key row l32 of the group; accumulator rows d = 32 dt + 8 g4 + 4 h + e -> chunk 8 dt + 2 g4 + h
         if (qh == 0) {
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int o = soff(l32, 8 * dt + 2 * g4 + h);
+                    const int o = soff(l32e, 8 * dt + 2 * g4 + he);
                     *reinterpret_cast<f32x4*>(kb + o) =
                         f32x4{dkacc[dt][4 * g4], dkacc[dt][4 * g4 + 1], dkacc[dt][4 * g4 + 2], dkacc[dt][4 * g4 + 3]};
                     *reinterpret_cast<f32x4*>(vb + o) =
@@ -610,7 +627,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
             for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int o = soff(l32, 8 * dt + 2 * g4 + h);
+                    const int o = soff(l32e, 8 * dt + 2 * g4 + he);
                     f32x4 pk = *reinterpret_cast<const f32x4*>(kb + o);
                     f32x4 pv = *reinterpret_cast<const f32x4*>(vb + o);
 #pragma unroll
@@ -629,7 +646,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         static_assert(TOTAL % THREADS == 0, "whole passes");
 #pragma unroll
         for (int pass = 0; pass < TOTAL / THREADS; ++pass) {
-            const int c = pass * THREADS + tid;
+            const int c = pass * THREADS + tid_e;
             const int row = c / CPR, ch = c - row * CPR;
             const int key = k0 + row;
             const int o = soff(row & 31, ch);
@@ -650,6 +667,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                 }
             }
         }
+    }
+    __syncthreads();                                    // the staging rows are read; LDS free for the next item
     }
 }
 
@@ -885,16 +904,22 @@ static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void
                          long mhead, hipStream_t st)
 {
     const int nkblk = (N + BwdKVCfg<D>::BN - 1) / BwdKVCfg<D>::BN;
-    const dim3 grid(nkblk * BH), block(64 * BwdKVCfg<D>::WAVES);
+    const int nitems = nkblk * BH;
+    const bool split = CAUSAL ? (BH & 7) == 0 : (nitems & 7) == 0;
+    int ncu = 0;
+    if (hipError_t e = device_cu_count(&ncu); e != hipSuccess) return e;
+    int nwg = nitems < ncu ? nitems : ncu;                 // one workgroup per CU
+    if (split) nwg &= ~7;                                   // whole XCD rows (nitems >= 8 here)
+    const dim3 grid(nwg), block(64 * BwdKVCfg<D>::WAVES);
     const int slots = tune_lookup(kTuneDkdv, D, CAUSAL, N).slots;
     if (bmask)
         hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G, true>), grid, block, 0, st, (const bf16*)Q, (const bf16*)K,
                            (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, bmask, mhead,
-                           slots);
+                           slots, nitems);
     else
         hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, G, false>), grid, block, 0, st, (const bf16*)Q, (const bf16*)K,
                            (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dK, (G*)dV, N, nkblk, scale, nullptr, 0L,
-                           slots);
+                           slots, nitems);
     return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace attn {
 
 typedef __bf16 bf16;
@@ -276,6 +278,24 @@ __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Compute units of the current device, looked up once per device (persistent grids
+// are sized by it).
+inline hipError_t device_cu_count(int* n)
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    int v = (dev >= 0 && dev < 64) ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (v == 0) {
+        if (hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev); e != hipSuccess)
+            return e;
+        if (v < 1) return hipErrorInvalidDevice;
+        if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+    }
+    *n = v;
+    return hipSuccess;
+}
 
 // Workgroup index -> logical index so that consecutive logical indices (the
 // blocks of one head) run on the same XCD and share its L2.  Hardware hands
