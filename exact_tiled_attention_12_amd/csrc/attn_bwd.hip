@@ -430,20 +430,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     const int kg = wave & 3, qh = wave >> 2;            // key group, query half
     const int l32 = lane & 31, h = lane >> 5;
 
-    // Persistent grid (one workgroup per CU): each workgroup walks its share of the
-    // nitems (head, key block) items, taken in the order block_coords gives an XCD.
-    // Workgroup c of an XCD (of P there) takes positions c, 2P-1-c, 2P+c, 4P-1-c, ...
-    // of that XCD's sequence, so a heavy causal item pairs with a light one.
-    const bool split = CAUSAL ? ((nitems / nkblk) & 7) == 0 : (nitems & 7) == 0;
-    const int xcd = split ? (int)(blockIdx.x & 7) : 0;
-    const int pc = split ? (int)(blockIdx.x >> 3) : (int)blockIdx.x;
-    const int P = split ? (int)(gridDim.x >> 3) : (int)gridDim.x;
-    const int KX = split ? nitems >> 3 : nitems;
+    // persistent grid (one workgroup per CU) over the nitems (head, key block) items
+    ItemWalk walk;
+    walk.init(blockIdx.x, gridDim.x, nitems, items_split<CAUSAL>(nitems, nkblk));
     for (int t = 0;; ++t) {
-    const int pos = (t & 1) ? (t + 1) * P - 1 - pc : t * P + pc;
-    if (pos >= KX) break;
+    const int item = walk.item(t);
+    if (item < 0) break;
     int head, kb;
-    block_coords<CAUSAL, false>(split ? 8 * pos + xcd : pos, nitems, nkblk, slots, head, kb);
+    block_coords<CAUSAL, false>(item, nitems, nkblk, slots, head, kb);
     const int k0 = kb * C::BN;
     const int k0w = k0 + 32 * kg;
     const int mykey = k0w + l32;
@@ -905,11 +899,8 @@ static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void
 {
     const int nkblk = (N + BwdKVCfg<D>::BN - 1) / BwdKVCfg<D>::BN;
     const int nitems = nkblk * BH;
-    const bool split = CAUSAL ? (BH & 7) == 0 : (nitems & 7) == 0;
-    int ncu = 0;
-    if (hipError_t e = device_cu_count(&ncu); e != hipSuccess) return e;
-    int nwg = nitems < ncu ? nitems : ncu;                 // one workgroup per CU
-    if (split) nwg &= ~7;                                   // whole XCD rows (nitems >= 8 here)
+    int nwg = 0;
+    if (hipError_t e = persistent_grid(nitems, 1, items_split<CAUSAL>(nitems, nkblk), &nwg); e != hipSuccess) return e;
     const dim3 grid(nwg), block(64 * BwdKVCfg<D>::WAVES);
     const int slots = tune_lookup(kTuneDkdv, D, CAUSAL, N).slots;
     if (bmask)

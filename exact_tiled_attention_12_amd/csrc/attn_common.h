@@ -339,6 +339,52 @@ __device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int SLOT
     }
 }
 
+// Persistent grids: a kernel launches about as many workgroups as the GPU holds at once
+// and each walks a share of the nitems work items (the blocks block_coords numbers),
+// so no workgroup waits to be dispatched behind another.  The items of an XCD keep
+// block_coords's order (heavy causal blocks first); workgroup c of the P on an XCD takes
+// positions c, 2P-1-c, 2P+c, 4P-1-c, ... of that XCD's sequence, which pairs each heavy
+// item with a light one.  Without whole XCD rows (see block_coords) the GPU is one sequence.
+template <bool CAUSAL>
+__host__ __device__ __forceinline__ bool items_split(int nitems, int nblk)
+{
+    return CAUSAL ? ((nitems / nblk) & 7) == 0 : (nitems & 7) == 0;
+}
+
+struct ItemWalk {
+    int xcd, pc, P, KX;
+    bool split;
+    __device__ __forceinline__ void init(int bid, int nwg, int nitems, bool split_)
+    {
+        split = split_;
+        xcd = split ? (bid & 7) : 0;
+        pc = split ? (bid >> 3) : bid;
+        P = split ? (nwg >> 3) : nwg;
+        KX = split ? (nitems >> 3) : nitems;
+    }
+    // the item of step t of this workgroup, or -1 once its share is done
+    __device__ __forceinline__ int item(int t) const
+    {
+        const int pos = (t & 1) ? (t + 1) * P - 1 - pc : t * P + pc;
+        if (pos >= KX) return -1;
+        return split ? 8 * pos + xcd : pos;
+    }
+};
+
+// Workgroups of a persistent grid: per_cu resident workgroups on every CU, at most one
+// per item, whole XCD rows when the items split by XCD.
+inline hipError_t persistent_grid(int nitems, int per_cu, bool split, int* nwg)
+{
+    int ncu = 0;
+    if (hipError_t e = device_cu_count(&ncu); e != hipSuccess) return e;
+    int n = ncu * per_cu;
+    if (n > nitems) n = nitems;
+    if (split) n &= ~7;                                 // nitems is a multiple of 8 here
+    if (n < 1) n = 1;
+    *nwg = n;
+    return hipSuccess;
+}
+
 // ---------------------------------------------------------------------------
 // Block-sparse masks.  A mask is uint8 [T][T] per head, T = ceil(N / kMaskBlock):
 // entry (a, b) nonzero keeps the scores of query block a against key block b,
