@@ -475,18 +475,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         if (wave == 1) lreg = buf_ld4f(make_rsrc(Dg + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
     };
 
+    // One query block, ordered so that each wave's VALU work overlaps its own MFMAs:
+    //   S = Q K^T;  dP = dO V^T while P = exp2(S c2 - LSE log2 e) is computed (in place);
+    //   dV^T += dO^T P while dS = P o (dP - D) is computed;  dK^T += Q^T dS.
+    // Fragments are read PF MFMAs ahead through small rings; sched_barrier keeps each
+    // MFMA next to its slice of VALU work.
     auto block_body = [&](int i, const char* sQ, const char* sG, const float* sL, const float* sD) {
         const int q0 = i * C::BM;
-        // S and dP; their fragments (Q, K, dO, V rows in turn) are read PF ahead through a
-        // small ring (sched_barrier keeps the order)
+        constexpr int PF = 4, NKS = C::NKS, NDT = C::NDT;
         f32x16 sacc, pacc;
         {
-            constexpr int PF = 4, NF = 4 * C::NKS;
-            bf16x8 ring[PF];
+            constexpr int NF = 2 * NKS;                 // f: s = f / 2; A (Q rows), then B (K rows)
             auto frag = [&](int f) __attribute__((always_inline)) {
-                const int s = f >> 2, w = f & 3;
-                return tl.row(w == 0 ? sQ : w == 1 ? sK : w == 2 ? sG : sV, (w & 1) ? 32 * kg : 32 * qh, s);
+                return tl.row((f & 1) ? sK : sQ, (f & 1) ? 32 * kg : 32 * qh, f >> 1);
             };
+            bf16x8 ring[PF];
 #pragma unroll
             for (int f = 0; f < PF; ++f) ring[f] = frag(f);
 #pragma unroll
@@ -496,45 +499,94 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                     ring[f % PF] = frag(f + PF);
                     ring[(f + 1) % PF] = frag(f + PF + 1);
                 }
-                const int s = f >> 2;
-                if (f & 2)
-                    pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s == 0 ? f32x16{} : pacc, 0, 0, 0);
-                else
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s == 0 ? f32x16{} : sacc, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, f == 0 ? f32x16{} : sacc, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        {
+            constexpr int NF = 2 * NKS;                 // dO rows (A), V rows (B)
+            auto frag = [&](int f) __attribute__((always_inline)) {
+                return tl.row((f & 1) ? sV : sG, (f & 1) ? 32 * kg : 32 * qh, f >> 1);
+            };
+            bf16x8 ring[PF];
+#pragma unroll
+            for (int f = 0; f < PF; ++f) ring[f] = frag(f);
+            f32x4 l4[2];
+            l4[0] = *reinterpret_cast<const f32x4*>(sL + 32 * qh + 4 * h);
+#pragma unroll
+            for (int f = 0; f < NF; f += 2) {
+                const int s = f >> 1;
+                const bf16x8 a = ring[f % PF], b = ring[(f + 1) % PF];
+                if (f + PF < NF) {
+                    ring[f % PF] = frag(f + PF);
+                    ring[(f + 1) % PF] = frag(f + PF + 1);
+                }
+                pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, f == 0 ? f32x16{} : pacc, 0, 0, 0);
+                // P of score elements [16 s / NKS, 16 (s + 1) / NKS), in place; row group g4 = r / 4
+#pragma unroll
+                for (int r = 16 * s / NKS; r < 16 * (s + 1) / NKS; ++r) {
+                    const int g4 = r >> 2;
+                    if ((r & 3) == 0 && g4 + 1 < 4)     // the next group's -LSE log2 e, one group ahead
+                        l4[(g4 + 1) & 1] = *reinterpret_cast<const f32x4*>(sL + 32 * qh + 8 * (g4 + 1) + 4 * h);
+                    sacc[r] = fast_exp2(fmaf(sacc[r], c2, l4[g4 & 1][r & 3]));
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         // (a wave whose keys all follow its queries gets P = 0 from the mask; skipping
         // it instead would split the accumulators' live ranges)
-        const bool need_mask = CAUSAL && (q0 + 32 * qh < k0w + 31);
+        if (CAUSAL && (q0 + 32 * qh < k0w + 31)) {      // key > query -> 0
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (mykey > q0 + 32 * qh + 8 * (r >> 2) + 4 * h + (r & 3)) sacc[r] = 0.f;
+        }
         bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int qo = 32 * qh + 8 * g4 + 4 * h;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + qo);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + qo);
-            float p[4];
+        for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = to_bf16(sacc[r]);
+        // dV^T += dO^T P (products m = s2 * NDT + dt) while dS = P (dP - D) is computed
+        {
+            constexpr int NM = 2 * NDT;
+            auto frag = [&](int m) __attribute__((always_inline)) {
+                return tl.tr(sG, 32 * qh + 16 * (m / NDT), m % NDT);
+            };
+            bf16x8 ring[PF];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(sacc[4 * g4 + e], c2, l4[e]));
-            if (need_mask) {              // key > query -> 0
+            for (int m = 0; m < PF && m < NM; ++m) ring[m] = frag(m);
+            f32x4 d4[2];
+            d4[0] = *reinterpret_cast<const f32x4*>(sD + 32 * qh + 4 * h);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (mykey > q0 + qo + e) p[e] = 0.f;
-            }
+            for (int m = 0; m < NM; ++m) {
+                const bf16x8 a = ring[m % PF];
+                if (m + PF < NM) ring[m % PF] = frag(m + PF);
+                const int s2 = m / NDT, dt = m % NDT;
+                dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s2], dvacc[dt], 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pb[g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e]);
-                sb[g4 >> 1][4 * (g4 & 1) + e] = to_bf16(p[e] * (pacc[4 * g4 + e] - d4[e]));
+                for (int r = 16 * m / NM; r < 16 * (m + 1) / NM; ++r) {
+                    const int g4 = r >> 2;
+                    if ((r & 3) == 0 && g4 + 1 < 4)
+                        d4[(g4 + 1) & 1] = *reinterpret_cast<const f32x4*>(sD + 32 * qh + 8 * (g4 + 1) + 4 * h);
+                    sb[r >> 3][r & 7] = to_bf16(sacc[r] * (pacc[r] - d4[g4 & 1][r & 3]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // dK^T += Q^T dS
+        {
+            constexpr int NM = 2 * NDT;
+            auto frag = [&](int m) __attribute__((always_inline)) {
+                return tl.tr(sQ, 32 * qh + 16 * (m / NDT), m % NDT);
+            };
+            bf16x8 ring[PF];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+            for (int m = 0; m < PF && m < NM; ++m) ring[m] = frag(m);
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) {
-                const int k0q = 32 * qh + 16 * s2;
-                dvacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sG, k0q, dt), pb[s2], dvacc[dt], 0, 0, 0);
-                dkacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sQ, k0q, dt), sb[s2], dkacc[dt], 0, 0, 0);
+            for (int m = 0; m < NM; ++m) {
+                const bf16x8 a = ring[m % PF];
+                if (m + PF < NM) ring[m % PF] = frag(m + PF);
+                dkacc[m % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[m / NDT], dkacc[m % NDT], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
     };
 
     if constexpr (!SPARSE) {
