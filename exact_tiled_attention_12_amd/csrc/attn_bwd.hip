@@ -951,8 +951,13 @@ static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void
 {
     const int nkblk = (N + BwdKVCfg<D>::BN - 1) / BwdKVCfg<D>::BN;
     const int nitems = nkblk * BH;
-    int nwg = 0;
-    if (hipError_t e = persistent_grid(nitems, 1, items_split<CAUSAL>(nitems, nkblk), &nwg); e != hipSuccess) return e;
+    // Dense: a persistent grid.  Block-sparse: one workgroup per item, since a mask makes the
+    // items' costs unrelated to the static heavy-first order and the hardware's dynamic dispatch
+    // balances them better (with nwg = nitems every workgroup walks exactly its own item).
+    int nwg = nitems;
+    if (!bmask)
+        if (hipError_t e = persistent_grid(nitems, 1, items_split<CAUSAL>(nitems, nkblk), &nwg); e != hipSuccess)
+            return e;
     const dim3 grid(nwg), block(64 * BwdKVCfg<D>::WAVES);
     const int slots = tune_lookup(kTuneDkdv, D, CAUSAL, N).slots;
     if (bmask)
