@@ -205,3 +205,25 @@ def test_long_sequence_sampled():
         _say(f"  head {hh}:", {n: f"{e:.2e}" for n, e in errs.items()})
         for n, e in errs.items():
             assert e <= TOL["bf16"], f"head {hh} {n}: {e}"
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_key_side_walk_uneven_heads(causal):
+    """B1 H3 N = 11000 d = 64: 86 key blocks x 3 heads = 258 (head, key block) items, more than
+    the GPU has CUs and with B*H not a multiple of 8, so the key side's persistent grid walks
+    one GPU-wide sequence and some workgroups take two items (the lightest blocks of the last
+    heads).  Sampled key rows (dK, dV) of every head, the last 300 keys among them."""
+    N = 11000
+    _say(f"case key-side walk, uneven heads, causal={causal}")
+    q, k, v, do = make_inputs(1, 3, N, 64, "bf16", seed=110 + causal)
+    o, lse, (dq, dk, dv) = _run(q, k, v, do, causal)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 127, 128, 5000, N - 300, N - 129, N - 1], rng.integers(N - 300, N, 6),
+                                     rng.integers(0, N, 4)]))
+    ridx = torch.as_tensor(rows)
+    for hh in range(3):
+        dKc, dVc = oracle.cols(q[0, hh], k[0, hh], v[0, hh], do[0, hh], rows, causal=causal)
+        errs = {"dK": _err(dk[0, hh][ridx], dKc), "dV": _err(dv[0, hh][ridx], dVc)}
+        _say(f"  head {hh}:", {n: f"{e:.2e}" for n, e in errs.items()})
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], f"head {hh} {n}: {e}"
