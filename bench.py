@@ -223,8 +223,10 @@ def load_traffic(kernel):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU's clocks take about 20 steps (~30 ms of this load) to settle: the first steps of a process
+    # run 5-15% slower, so the default warmup covers them
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-secondary", action="store_true", help="skip the N=16k measurement")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
