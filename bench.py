@@ -38,7 +38,8 @@ KERNEL_SOURCES = ["exact_tiled_attention_12_amd/csrc/attn_fwd.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_bwd.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_fwd_fp8.hip",
                   "exact_tiled_attention_12_amd/csrc/attn_common.h",
-                  "exact_tiled_attention_12_amd/csrc/attn_tuning.h"]
+                  "exact_tiled_attention_12_amd/csrc/attn_tuning.h",
+                  "exact_tiled_attention_12_amd/build.py"]          # (the compiler flags)
 
 
 def source_hash():

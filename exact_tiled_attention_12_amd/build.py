@@ -11,7 +11,10 @@ SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_fwd_fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU forms are kept out of the device code on purpose.
+# -amdgpu-set-wave-priority: the backend raises a wave's priority until its first vector-memory
+# loads are issued (measured 0.5-1% faster on the forward and key-side kernels)
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-mllvm", "-amdgpu-set-wave-priority",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
          "-I", os.path.join(ROOT, "include")]
