@@ -241,7 +241,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (asked for {args.gpus}); "
               "heads shard across GPUs with no exchange, but no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
