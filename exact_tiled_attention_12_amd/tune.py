@@ -104,8 +104,14 @@ def time_cases(lib_path, reps=20, warmup=5):
             else:
                 dq = torch.empty(q.shape, device=dev)
                 run = lambda: attn.attn_bwd_dq(q, k, v, do, lse, D, causal=causal, dq=dq)
-        for _ in range(warmup):
+        # warm up for at least 60 ms of this load: a fresh process's first ~30 ms run at lower clocks
+        t0 = time.time()
+        n = 0
+        while n < warmup or time.time() - t0 < 0.06:
             run()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
