@@ -126,3 +126,17 @@ def test_matches_bf16_kernel_on_same_values_statistically():
     _say(f"  mean |O8 - O16| {diff.mean().item():.2e}, max {diff.max().item():.2e}, "
          f"LSE max {(l8 - lb).abs().max().item():.2e}")
     assert diff.mean().item() < 2.0 ** -4 / math.sqrt(64) * float(vb.float().abs().mean())
+
+
+def test_beyond_4096_causal():
+    """B1 H2 N4500 d128 causal: past N = 4096 the launch table gives the causal d = 128 fp8
+    forward its 128-key tile; both heads checked in full against the bound."""
+    _say("case fp8 B1 H2 N4500 d128 causal (128-key tiles)")
+    dev = _dev()
+    (q8, k8, v8), (sq, sk, sv) = make_fp8_inputs(1, 2, 4500, 128, seed=45)
+    o, lse = attn_fwd_fp8(q8.to(dev), k8.to(dev), v8.to(dev), sq, sk, sv, causal=True)
+    torch.cuda.synchronize()
+    for hh in range(2):
+        r = _check_head(o[0, hh].cpu(), lse[0, hh].cpu(), _real(q8[0, hh], sq), _real(k8[0, hh], sk),
+                        _real(v8[0, hh], sv), True)
+        _say(f"  head {hh}: O max {r[0]:.2e} mean {r[1]:.2e}, LSE max {r[2]:.2e}")
