@@ -105,6 +105,22 @@ def test_scale_edge_values(scale):
     _check_full(q, k, v, do, False, "bf16", scale=scale, relative=True)
 
 
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores(d, causal):
+    """Scores that keep growing along the keys, so the running row max moves far past its
+    reference on later tiles, in the first and in the second 32-key half of a tile: key
+    rows are scaled by a ramp (1 + j/48), with extra factors on keys 96-127 and 320-351."""
+    N = 700
+    _say(f"case rising scores d={d} causal={causal} N={N}")
+    q, k, v, do = make_inputs(1, 2, N, d, "bf16", seed=300 + d + causal)
+    ramp = 1.0 + torch.arange(N, dtype=torch.float32) / 48.0
+    ramp[96:128] *= 3.0
+    ramp[320:352] *= 2.0
+    k = (k.float() * ramp[:, None]).to(torch.bfloat16)
+    _check_full(q, k, v, do, causal, "bf16", relative=True)
+
+
 def test_bf16_gradients_option():
     _say("case bf16 grads")
     q, k, v, do = make_inputs(1, 2, 300, 128, "bf16", seed=9)
