@@ -448,12 +448,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     TileLane<RB, C::NKS, C::NDT, false> tl;
     tl.init(lane);
 
-    // the workgroup's K and V rows to LDS (16 rows per wave each)
-    {
-        const uint32_t bytes = (uint32_t)(N - k0) * ROWB;
-        dma_rows<D, RB, false>(make_rsrc(K + hoff + (size_t)k0 * D, bytes), sK, wave * (C::BN / 8), C::BN / 8, lane);
-        dma_rows<D, RB, false>(make_rsrc(V + hoff + (size_t)k0 * D, bytes), sV, wave * (C::BN / 8), C::BN / 8, lane);
-    }
+    // the workgroup's K and V rows to LDS (16 rows per wave each); after the first item
+    // the previous item's epilogue has already issued them
+    auto issue_kv = [&](size_t ho, int kk0) {
+        const uint32_t bytes = (uint32_t)(N - kk0) * ROWB;
+        int lane_k = lane;                              // opaque: offsets computed here, not held in registers
+        asm volatile("" : "+v"(lane_k));
+        dma_rows<D, RB, false>(make_rsrc(K + ho + (size_t)kk0 * D, bytes), sK, wave * (C::BN / 8), C::BN / 8, lane_k);
+        dma_rows<D, RB, false>(make_rsrc(V + ho + (size_t)kk0 * D, bytes), sV, wave * (C::BN / 8), C::BN / 8, lane_k);
+    };
+    if (t == 0) issue_kv(hoff, k0);
 
     f32x16 dvacc[C::NDT], dkacc[C::NDT];
 #pragma unroll
@@ -635,86 +639,82 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
 
     // Epilogue.  The two query halves' partials are summed in LDS, row-major (one key per
     // row, DP floats, 16-byte chunks XOR-swizzled by the row so that the MFMA-layout writes
-    // and the row reads are free of bank conflicts): dK rows of key group g in the g-th
-    // Q/dO buffer, dV rows in the K/V tiles.  Then all eight waves store whole rows, so
-    // each store instruction writes contiguous memory.
+    // and the row reads are free of bank conflicts), key group g's rows in the g-th Q/dO
+    // buffer: dV first, then dK.  After each sum all eight waves store whole rows, so each
+    // store instruction writes contiguous memory.  The K/V tiles are free from the start of
+    // the epilogue, so the next item's K and V rows are issued first and load meanwhile.
     wait_vmem_all();
     __syncthreads();                                    // every tile fully read
     {
+        const int nitem = walk.item(t + 1);
+        if (nitem >= 0) {
+            int nhead, nkb;
+            block_coords<CAUSAL, false>(nitem, nitems, nkblk, slots, nhead, nkb);
+            issue_kv((size_t)nhead * (size_t)N * D, nkb * C::BN);
+        }
+    }
+    {
         constexpr int NCHP = C::DP / 4 <= 16 ? 16 : 32;  // 16-byte chunks per LDS row (power of two)
         constexpr int GROUP_BYTES = 32 * NCHP * 16;      // one key group's rows
-        static_assert(GROUP_BYTES <= C::Q_BYTES && 2 * GROUP_BYTES <= C::K_BYTES, "epilogue staging fits");
+        static_assert(GROUP_BYTES <= C::Q_BYTES, "epilogue staging fits");
         auto kbuf = [&](int g) -> char* { return g == 0 ? sQ0 : g == 1 ? sQ1 : g == 2 ? sG0 : sG1; };
-        auto vbuf = [&](int g) -> char* { return (g < 2 ? sK : sV) + (g & 1) * GROUP_BYTES; };
         auto soff = [](int row, int ch) { return (row * NCHP + (ch ^ (row & 15))) * 16; };
         char* kb = kbuf(kg);
-        char* vb = vbuf(kg);
         // lane index made opaque here, so that the offsets below are computed per item and
         // not hoisted out of the item loop (where they would sit in registers the main loop needs)
         int lane_e = lane;
         asm volatile("" : "+v"(lane_e));
         const int l32e = lane_e & 31, he = lane_e >> 5, tid_e = 64 * wave + lane_e;
-        // lane: key row l32 of the group; accumulator rows d = 32 dt + 8 g4 + 4 h + e -> chunk 8 dt + 2 g4 + h
-        if (qh == 0) {
+        auto sum_store = [&](const f32x16 (&acc)[C::NDT], G* __restrict__ dst, float mult) {
+            // lane: key row l32 of the group; accumulator rows d = 32 dt + 8 g4 + 4 h + e -> chunk 8 dt + 2 g4 + h
+            if (qh == 0) {
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
+                for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int o = soff(l32e, 8 * dt + 2 * g4 + he);
-                    *reinterpret_cast<f32x4*>(kb + o) =
-                        f32x4{dkacc[dt][4 * g4], dkacc[dt][4 * g4 + 1], dkacc[dt][4 * g4 + 2], dkacc[dt][4 * g4 + 3]};
-                    *reinterpret_cast<f32x4*>(vb + o) =
-                        f32x4{dvacc[dt][4 * g4], dvacc[dt][4 * g4 + 1], dvacc[dt][4 * g4 + 2], dvacc[dt][4 * g4 + 3]};
-                }
-        }
-        __syncthreads();
-        if (qh == 1) {
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        *reinterpret_cast<f32x4*>(kb + soff(l32e, 8 * dt + 2 * g4 + he)) =
+                            f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
+            }
+            __syncthreads();
+            if (qh == 1) {
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
+                for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int o = soff(l32e, 8 * dt + 2 * g4 + he);
-                    f32x4 pk = *reinterpret_cast<const f32x4*>(kb + o);
-                    f32x4 pv = *reinterpret_cast<const f32x4*>(vb + o);
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int o = soff(l32e, 8 * dt + 2 * g4 + he);
+                        f32x4 pk = *reinterpret_cast<const f32x4*>(kb + o);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pk[e] += dkacc[dt][4 * g4 + e];
-                        pv[e] += dvacc[dt][4 * g4 + e];
+                        for (int e = 0; e < 4; ++e) pk[e] += acc[dt][4 * g4 + e];
+                        *reinterpret_cast<f32x4*>(kb + o) = pk;
                     }
-                    *reinterpret_cast<f32x4*>(kb + o) = pk;
-                    *reinterpret_cast<f32x4*>(vb + o) = pv;
-                }
-        }
-        __syncthreads();
-        // dK = scale * (dK^T acc)^T, dV = (dV^T acc)^T: D/4 chunks per key row, consecutive threads
-        // take consecutive chunks of a row
-        constexpr int CPR = D / 4, TOTAL = C::BN * CPR, THREADS = 64 * C::WAVES;
-        static_assert(TOTAL % THREADS == 0, "whole passes");
+            }
+            __syncthreads();
+            // D/4 chunks per key row, consecutive threads take consecutive chunks of a row
+            constexpr int CPR = D / 4, TOTAL = C::BN * CPR, THREADS = 64 * C::WAVES;
+            static_assert(TOTAL % THREADS == 0, "whole passes");
 #pragma unroll
-        for (int pass = 0; pass < TOTAL / THREADS; ++pass) {
-            const int c = pass * THREADS + tid_e;
-            const int row = c / CPR, ch = c - row * CPR;
-            const int key = k0 + row;
-            const int o = soff(row & 31, ch);
-            const f32x4 a = *reinterpret_cast<const f32x4*>(kbuf(row >> 5) + o);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(vbuf(row >> 5) + o);
-            if (key < N) {
-                G* pk = dK + hoff + (size_t)key * D + 4 * ch;
-                G* pv = dV + hoff + (size_t)key * D + 4 * ch;
-                if constexpr (sizeof(G) == 4) {
-                    *reinterpret_cast<f32x4*>(pk) = a * scale;
-                    *reinterpret_cast<f32x4*>(pv) = b;
-                } else {
-                    bf16x4 x, y;
+            for (int pass = 0; pass < TOTAL / THREADS; ++pass) {
+                const int c = pass * THREADS + tid_e;
+                const int row = c / CPR, ch = c - row * CPR;
+                const int key = k0 + row;
+                const f32x4 a = *reinterpret_cast<const f32x4*>(kbuf(row >> 5) + soff(row & 31, ch));
+                if (key < N) {
+                    G* pk = dst + hoff + (size_t)key * D + 4 * ch;
+                    if constexpr (sizeof(G) == 4) {
+                        *reinterpret_cast<f32x4*>(pk) = a * mult;
+                    } else {
+                        bf16x4 x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) { x[e] = to_bf16(a[e] * scale); y[e] = to_bf16(b[e]); }
-                    *reinterpret_cast<bf16x4*>(pk) = x;
-                    *reinterpret_cast<bf16x4*>(pv) = y;
+                        for (int e = 0; e < 4; ++e) x[e] = to_bf16(a[e] * mult);
+                        *reinterpret_cast<bf16x4*>(pk) = x;
+                    }
                 }
             }
-        }
+            __syncthreads();                            // the staging rows are read
+        };
+        sum_store(dvacc, dV, 1.0f);                     // dV = (dV^T acc)^T
+        sum_store(dkacc, dK, scale);                    // dK = scale * (dK^T acc)^T
     }
-    __syncthreads();                                    // the staging rows are read; LDS free for the next item
     }
 }
 
