@@ -1,8 +1,8 @@
 """Benchmark of the attention hot path on one MI355X.
 
-One step = forward (attn_fwd) + backward preprocess (attn_bwd_preprocess) +
-key-side backward (attn_bwd_dkdv) + query-side backward (attn_bwd_dq) over one
-batch of resident synthetic inputs: the whole path, fwd and bwd.  Default workload: B=4, H=16, N=4096,
+One step = forward (attn_fwd) + query-side backward with the preprocess folded in
+(attn_bwd_dq_d: dQ and D) + key-side backward (attn_bwd_dkdv), the order attn_bwd
+takes for bf16, over one batch of resident synthetic inputs: the whole path, fwd and bwd.  Default workload: B=4, H=16, N=4096,
 d=128, causal, bf16 (the N = 4k case of the headline metric); the N = 16k case
 (B=1, H=16) is measured in the same run and reported under "secondary", and the
 same N = 16k shape with a local + global block mask under "block_sparse".
@@ -24,8 +24,8 @@ sys.path.insert(0, ROOT)
 
 import torch  # noqa: E402
 
-from exact_tiled_attention_12_amd import (attn_bwd_blocksparse, attn_bwd_dkdv, attn_bwd_dq,  # noqa: E402
-                                          attn_bwd_preprocess, attn_fwd, attn_fwd_blocksparse, attn_fwd_fp8)
+from exact_tiled_attention_12_amd import (attn_bwd_blocksparse, attn_bwd_dkdv, attn_bwd_dq_d,  # noqa: E402
+                                          attn_fwd, attn_fwd_blocksparse, attn_fwd_fp8)
 from exact_tiled_attention_12_amd.configs import CONFIGS  # noqa: E402
 from exact_tiled_attention_12_amd.flops import attn_flops, blocksparse_flops  # noqa: E402
 from exact_tiled_attention_12_amd.inputs import config_inputs, local_global_mask, make_fp8_inputs  # noqa: E402
@@ -69,7 +69,7 @@ class Workload:
         self.fl_fwd = attn_flops(B, H, N, d, cfg.causal, "fwd")
         self.fl_bwd = attn_flops(B, H, N, d, cfg.causal, "bwd")
 
-    KERNELS = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
+    KERNELS = ("attn_fwd", "attn_bwd_dq_d", "attn_bwd_dkdv")
 
     def step(self, ev=None):
         c = self.cfg
@@ -79,12 +79,10 @@ class Workload:
         rec(1)
         if not c.backward:
             return
-        attn_bwd_preprocess(self.o, self.do, D=self.D)
+        attn_bwd_dq_d(self.q, self.k, self.v, self.o, self.do, self.lse, D=self.D, causal=c.causal, dq=self.dq)
         rec(2)
         attn_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.D, causal=c.causal, dk=self.dk, dv=self.dv)
         rec(3)
-        attn_bwd_dq(self.q, self.k, self.v, self.do, self.lse, self.D, causal=c.causal, dq=self.dq)
-        rec(4)
 
     def measure(self, steps, warmup):
         """Returns (wall seconds per step, {kernel: mean seconds per launch})."""
@@ -284,7 +282,7 @@ def main():
     # algorithmic FLOPs per launch: forward 4 N^2 d per head; the backward's 2.5x
     # split as the key side's 4 products (2.0x) and the query side's 3 (1.5x)
     # minus the recomputed S and dP both sides share (counted once, on the key side)
-    kflops = {"attn_fwd": w.fl_fwd, "attn_bwd_dkdv": 2.0 * w.fl_fwd, "attn_bwd_dq": 0.5 * w.fl_fwd}
+    kflops = {"attn_fwd": w.fl_fwd, "attn_bwd_dkdv": 2.0 * w.fl_fwd, "attn_bwd_dq_d": 0.5 * w.fl_fwd}
     kern = {}
     for name, t in per.items():
         ent = {"us": round(t * 1e6, 2)}

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 ATTN_F32, ATTN_BF16 = 0, 1
 
-EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
+EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_d", "attn_bwd_main",
             "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
             "attn_fwd_fp8", "attn_status_str", "attn_last_hip_error")
 MASK_BLOCK = 128        # ATTN_MASK_BLOCK: rows and keys per block-mask entry
@@ -56,6 +56,7 @@ def lib():
         L.attn_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, vp]
         L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
         L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
+        L.attn_bwd_dq_d.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
         L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp]
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = sz
@@ -64,7 +65,7 @@ def lib():
         L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, vp, i, vp,
                                            sz, vp]
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, i, i, i, i, f, i, vp, vp, vp]
-        for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_main",
+        for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_d", "attn_bwd_main",
                      "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse", "attn_fwd_fp8"):
             getattr(L, name).restype = i
         L.attn_status_str.argtypes = [i]
@@ -170,6 +171,24 @@ def attn_bwd_dq(q, k, v, do, lse, D, scale=None, causal=False, dq=None, stream=N
     _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(dq), _stream(q, stream))
     return dq
+
+
+def attn_bwd_dq_d(q, k, v, o, do, lse, D=None, scale=None, causal=False, dq=None, stream=None):
+    """(dQ, D): dQ (fp32, written once) with the preprocess folded in: D = rowsum(dO o O) is
+    computed per query row, used, and returned for an attn_bwd_dkdv call.  bf16 inputs only."""
+    B, H, N, d = _shape(q)
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("o must match q in shape and dtype")
+    if D is None:
+        D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif D.shape != (B, H, N) or D.dtype != torch.float32:
+        raise ValueError("D must be fp32 [B, H, N]")
+    _check_inputs(q, k, v, o, do, lse, D)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = _grad(dq, q)
+    _call("attn_bwd_dq_d", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
+          float(scale), int(bool(causal)), _ptr(D), _ptr(dq), _stream(q, stream))
+    return dq, D
 
 
 def attn_bwd_main(q, k, v, do, lse, D, scale=None, causal=False, dq=None, dk=None, dv=None, stream=None):

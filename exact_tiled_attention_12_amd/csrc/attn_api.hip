@@ -105,7 +105,19 @@ attn_status attn_bwd_dq(const void* Q, const void* K, const void* V, const void*
     if (s != ATTN_OK) return s;
     if (!aligned16(dQ)) return ATTN_EINVAL;
     if (dt != ATTN_BF16) return ATTN_EUNSUPPORTED;
-    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false, nullptr, 0,
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, const_cast<float*>(D), nullptr, B * H, N, d, scale,
+                                        causal, dQ, false, nullptr, 0, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_dq_d(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                          const float* LSE, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                          float* D, float* dQ, void* stream)
+{
+    attn_status s = check_bwd_args(Q, K, V, dO, LSE, D, dt, B, H, N, d, scale, causal);
+    if (s != ATTN_OK) return s;
+    if (!aligned16(O) || !aligned16(dQ)) return ATTN_EINVAL;
+    if (dt != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, O, B * H, N, d, scale, causal, dQ, false, nullptr, 0,
                                         (hipStream_t)stream));
 }
 
@@ -123,7 +135,8 @@ attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const voi
     attn_status r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dK, dV, false,
                                                    nullptr, 0, st));
     if (r != ATTN_OK) return r;
-    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, D, B * H, N, d, scale, causal, dQ, false, nullptr, 0, st));
+    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, const_cast<float*>(D), nullptr, B * H, N, d, scale, causal,
+                                        dQ, false, nullptr, 0, st));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d)
@@ -148,16 +161,18 @@ static attn_status bwd_all(const void* Q, const void* K, const void* V, const vo
     const bool bf_in = dt == ATTN_BF16, bf_grad = grad_dt == ATTN_BF16;
     const int BH = B * H;
     float* Dd = static_cast<float*>(workspace);
-    attn_status r = from_hip(attn::launch_bwd_pre(O, dO, bf_in, BH, N, d, Dd, st));
-    if (r != ATTN_OK) return r;
-    if (!bf_in)
+    if (!bf_in) {
+        attn_status r = from_hip(attn::launch_bwd_pre(O, dO, bf_in, BH, N, d, Dd, st));
+        if (r != ATTN_OK) return r;
         return from_hip(attn::launch_bwd_f32(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, (float*)dQ, (float*)dK,
                                              (float*)dV, bmask, mhead, st));
-    r = from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dK, dV, bf_grad, bmask, mhead,
-                                       st));
+    }
+    // bf16: the dQ kernel also computes D (the preprocess) for its rows; the key side reads it
+    attn_status r = from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, Dd, O, BH, N, d, scale, causal, dQ, bf_grad, bmask,
+                                                 mhead, st));
     if (r != ATTN_OK) return r;
-    return from_hip(attn::launch_bwd_dq(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dQ, bf_grad, bmask, mhead,
-                                        st));
+    return from_hip(attn::launch_bwd_dkdv(Q, K, V, dO, LSE, Dd, BH, N, d, scale, causal, dK, dV, bf_grad, bmask,
+                                          mhead, st));
 }
 
 attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

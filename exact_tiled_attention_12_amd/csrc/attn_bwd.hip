@@ -742,9 +742,10 @@ struct BwdQCfg {
 template <int D, bool CAUSAL, typename G, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                       const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                                                      const float* __restrict__ LSE, const float* __restrict__ Dg,
-                                                      G* __restrict__ dQ, int N, int nqblk, float scale,
-                                                      const uint8_t* __restrict__ bmask, long mhead, int slots)
+                                                      const float* __restrict__ LSE, float* __restrict__ Dg,
+                                                      const bf16* __restrict__ Og, G* __restrict__ dQ, int N,
+                                                      int nqblk, float scale, const uint8_t* __restrict__ bmask,
+                                                      long mhead, int slots)
 {
     using C = BwdQCfg<D>;
     static_assert(kMaskBlock == C::BM && kMaskBlock == 2 * C::BN, "mask block = query block");
@@ -782,7 +783,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
             gf[s] = __builtin_bit_cast(bf16x8, buf_ld16(rg, ro + 32 * s));
         }
         nlse = -kLog2e * buf_ld4f(make_rsrc(LSE + (size_t)head * N, (uint32_t)N * 4), myq * 4);
-        dq_d = buf_ld4f(make_rsrc(Dg + (size_t)head * N, (uint32_t)N * 4), myq * 4);
+        if (Og != nullptr) {
+            // D = rowsum(dO o O) from this lane's half row of O and the dO fragments, written for
+            // the key-side kernel (rows past N read as zeros and are not written)
+            const auto ro_o = make_rsrc(Og + hoff, hb);
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < C::NKS; ++s) {
+                const bf16x8 o = __builtin_bit_cast(bf16x8, buf_ld16(ro_o, ro + 32 * s));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)gf[s][e], acc);
+            }
+            dq_d = acc + xor32(acc);
+            if (h == 0 && myq < N) Dg[(size_t)head * N + myq] = dq_d;
+        } else {
+            dq_d = buf_ld4f(make_rsrc(Dg + (size_t)head * N, (uint32_t)N * 4), myq * 4);
+        }
     }
 
     f32x16 dqacc[C::NDT];
@@ -972,20 +988,20 @@ static hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void
 }
 
 template <int D, bool CAUSAL, typename G>
-static hipError_t dq_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                       const float* Dd, int BH, int N, float scale, void* dQ, const uint8_t* bmask, long mhead,
+static hipError_t dq_t(const void* Q, const void* K, const void* V, const void* dO, const float* LSE, float* Dd,
+                       const void* O, int BH, int N, float scale, void* dQ, const uint8_t* bmask, long mhead,
                        hipStream_t st)
 {
     const int nqblk = (N + BwdQCfg<D>::BM - 1) / BwdQCfg<D>::BM;
     const int slots = tune_lookup(kTuneDq, D, CAUSAL, N).slots;
     if (bmask)
         hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G, true>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
-                           (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale, bmask,
-                           mhead, slots);
+                           (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (const bf16*)O, (G*)dQ, N,
+                           nqblk, scale, bmask, mhead, slots);
     else
         hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL, G, false>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
-                           (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (G*)dQ, N, nqblk, scale,
-                           nullptr, 0L, slots);
+                           (const bf16*)K, (const bf16*)V, (const bf16*)dO, LSE, Dd, (const bf16*)O, (G*)dQ, N,
+                           nqblk, scale, nullptr, 0L, slots);
     return hipGetLastError();
 }
 
@@ -1010,11 +1026,11 @@ hipError_t launch_bwd_dkdv(const void* Q, const void* K, const void* V, const vo
     ATTN_DISPATCH_D_CAUSAL_G(dkdv_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dK, dV, bmask, mhead, st)
 }
 
-hipError_t launch_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                         const float* Dd, int BH, int N, int d, float scale, int causal, void* dQ, bool bf16_grad,
+hipError_t launch_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE, float* Dd,
+                         const void* O, int BH, int N, int d, float scale, int causal, void* dQ, bool bf16_grad,
                          const uint8_t* bmask, long mhead, hipStream_t st)
 {
-    ATTN_DISPATCH_D_CAUSAL_G(dq_t, Q, K, V, dO, LSE, Dd, BH, N, scale, dQ, bmask, mhead, st)
+    ATTN_DISPATCH_D_CAUSAL_G(dq_t, Q, K, V, dO, LSE, Dd, O, BH, N, scale, dQ, bmask, mhead, st)
 }
 
 template <int D, bool CAUSAL>

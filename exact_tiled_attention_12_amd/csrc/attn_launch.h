@@ -23,8 +23,10 @@ hipError_t launch_bwd_pre(const void* O, const void* dO, bool bf16_in, int BH, i
 hipError_t launch_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
                            const float* D, int BH, int N, int d, float scale, int causal, void* dK, void* dV,
                            bool bf16_grad, const uint8_t* bmask, long mhead, hipStream_t st);
-hipError_t launch_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
-                         const float* D, int BH, int N, int d, float scale, int causal, void* dQ, bool bf16_grad,
+// dQ with O == nullptr reads D; with O given it computes D = rowsum(dO o O) for its rows,
+// uses it and writes it to D (for a key-side launch that follows).
+hipError_t launch_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE, float* D,
+                         const void* O, int BH, int N, int d, float scale, int causal, void* dQ, bool bf16_grad,
                          const uint8_t* bmask, long mhead, hipStream_t st);
 
 // fp32 inputs: zero dQacc, then one kernel for all three gradients (dQ by atomics).

@@ -91,6 +91,18 @@ attn_status attn_bwd_dq(const void* Q, const void* K, const void* V, const void*
                         int B, int H, int N, int d, float scale, int causal,
                         float* dQ, void* stream);
 
+/* Backward, query side with the preprocess folded in: like attn_bwd_dq, but D
+ * is an output.  Each workgroup computes D_i = sum_k dO_ik O_ik (fp32) for its
+ * own query rows from O and the dO rows it loads anyway, uses it for dS, and
+ * writes it to D [B,H,N] for an attn_bwd_dkdv call that follows.  O: dtype dt
+ * (ATTN_BF16 only, else ATTN_EUNSUPPORTED), 16-byte aligned.  This is the
+ * order attn_bwd takes for bf16 inputs: one pass over O and dO fewer than
+ * attn_bwd_preprocess + attn_bwd_dq. */
+attn_status attn_bwd_dq_d(const void* Q, const void* K, const void* V, const void* O,
+                          const void* dO, const float* LSE, attn_dtype dt,
+                          int B, int H, int N, int d, float scale, int causal,
+                          float* D, float* dQ, void* stream);
+
 /* Backward after the preprocess: dQ, dK, dV (fp32, written once).  bf16 inputs:
  * attn_bwd_dkdv then attn_bwd_dq.  fp32 inputs: one kernel for all three, with
  * dQ accumulated by fp32 atomics into dQ after zero-filling it. */
@@ -103,7 +115,9 @@ attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const voi
  * bytes.  Returns 0 for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
-/* Full backward = attn_bwd_preprocess + attn_bwd_main.  Q, K, V, O, dO: dtype
+/* Full backward.  bf16 inputs: attn_bwd_dq_d (dQ, and D into the workspace),
+ * then attn_bwd_dkdv.  fp32 inputs: attn_bwd_preprocess + attn_bwd_main.  The
+ * results do not depend on the order.  Q, K, V, O, dO: dtype
  * `dt`; LSE from attn_fwd with the same scale and causal flag.  dQ, dK, dV:
  * outputs of dtype grad_dt (ATTN_BF16 gradients need bf16 inputs, else
  * ATTN_EUNSUPPORTED).  workspace: device, 16-byte aligned, at least

@@ -75,6 +75,14 @@ def test_bwd_rejects_before_launch():
     assert L.attn_bwd_dkdv(P, P, P, P, P, P, attn.ATTN_F32, 1, 1, 16, 64, 0.1, 0, P, P, None) == attn.ATTN_EUNSUPPORTED
     assert L.attn_bwd_dq(P, P, P, P, P, P, attn.ATTN_F32, 1, 1, 16, 64, 0.1, 0, P, None) == attn.ATTN_EUNSUPPORTED
     assert L.attn_bwd_dq(P, P, P, P, P, NUL, attn.ATTN_BF16, 1, 1, 16, 64, 0.1, 0, P, None) == attn.ATTN_EINVAL
+    # dQ with the preprocess folded in: O (4th) and D (an output here) are checked like the rest
+    dq_d = lambda o=P, D=P, dt=attn.ATTN_BF16, d=64: L.attn_bwd_dq_d(P, P, P, o, P, P, dt, 1, 1, 16, d, 0.1, 0, D, P,
+                                                                     None)
+    assert dq_d(dt=attn.ATTN_F32) == attn.ATTN_EUNSUPPORTED
+    assert dq_d(o=MIS) == attn.ATTN_EINVAL
+    assert dq_d(o=NUL) == attn.ATTN_EINVAL
+    assert dq_d(D=NUL) == attn.ATTN_EINVAL
+    assert dq_d(d=96) == attn.ATTN_EUNSUPPORTED
 
 
 def test_blocksparse_rejects_bad_masks_before_launch():

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from exact_tiled_attention_12_amd import attn_bwd, attn_fwd
+from exact_tiled_attention_12_amd import attn_bwd, attn_bwd_dkdv, attn_bwd_dq_d, attn_fwd
 from exact_tiled_attention_12_amd.configs import CONFIGS
 from exact_tiled_attention_12_amd.inputs import config_inputs, make_inputs
 
@@ -119,6 +119,33 @@ def test_rising_scores(d, causal):
     ramp[320:352] *= 2.0
     k = (k.float() * ramp[:, None]).to(torch.bfloat16)
     _check_full(q, k, v, do, causal, "bf16", relative=True)
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_query_side_with_folded_preprocess(d, causal):
+    """attn_bwd_dq_d (dQ, and D = rowsum(dO o O) computed per query row) followed by
+    attn_bwd_dkdv on that D: gradients against the oracle, D against the fp64 row sums of
+    the same bf16 O and dO (fp32 accumulation bound)."""
+    N = 700
+    _say(f"case dq_d d={d} causal={causal} N={N}")
+    dev = _dev()
+    q, k, v, do = make_inputs(1, 3, N, d, "bf16", seed=500 + d + causal)
+    qg, kg, vg, dog = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = attn_fwd(qg, kg, vg, causal=causal)
+    D = torch.full(lse.shape, float("nan"), dtype=torch.float32, device=dev)
+    dq, D = attn_bwd_dq_d(qg, kg, vg, o, dog, lse, D=D, causal=causal)
+    dk, dv = attn_bwd_dkdv(qg, kg, vg, dog, lse, D, causal=causal)
+    torch.cuda.synchronize()
+    od = o.double().cpu() * do.double()
+    D_ref = od.sum(-1).numpy()
+    bound = 1e-5 * od.abs().sum(-1).numpy() + 1e-6
+    assert np.all(np.abs(D.double().cpu().numpy() - D_ref) <= bound)
+    for hh in range(3):
+        dQ, dK, dV = oracle.bwd(q[0, hh], k[0, hh], v[0, hh], do[0, hh], causal=causal)
+        errs = [_err(dq[0, hh], dQ), _err(dk[0, hh], dK), _err(dv[0, hh], dV)]
+        _say("  head", hh, [f"{e:.2e}" for e in errs])
+        assert max(errs) <= TOL["bf16"]
 
 
 def test_bf16_gradients_option():
