@@ -26,6 +26,8 @@
 // fwd_kernel_f32 (fp32 inputs, MFMA 32x32x2 f32) stages K and V through
 // registers into padded LDS (V transposed, key fastest); fwd_kernel_bf16 below
 // is the bf16 hot path.
+#include <float.h>
+
 #include "../../include/attn.h"
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -459,16 +461,16 @@ void fwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
             }
         }
 
-        // lane: query myq, keys kv0 + 32 kt + 8 (r/4) + 4 h + r%4
+        // lane: query myq, keys kv0 + 4 h + cr with cr = 32 kt + 8 (r/4) + r%4; a key is masked
+        // when it follows the query or lies past N, i.e. when cr exceeds one per-lane bound
         const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > q0w) || (kv0 + C::BN > N);
         if (need_mask) {
+            const int bound = CAUSAL ? min(myq, N - 1) - kv0 - 4 * h : N - 1 - kv0 - 4 * h;
 #pragma unroll
             for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if ((CAUSAL && key > myq) || key >= N) sacc[kt][r] = NEG_INF;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kt + 8 * (r >> 2) + (r & 3) > bound) sacc[kt][r] = NEG_INF;
         }
         float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
 #pragma unroll
@@ -489,7 +491,10 @@ void fwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                 for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
             mc = mnew;
         }
-        if (need_mask) {
+        // a masked score is -inf and c >= FLT_MIN, so exp2 gives 0 once mc is finite: a dense
+        // walk's first tile gives every row a key (key 0, or keys below N), so only
+        // block-sparse walks, whose rows may have seen no key yet, need the select
+        if (SPARSE && need_mask) {
 #pragma unroll
             for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
@@ -622,7 +627,8 @@ static hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, v
     const int nqblk = (N + C::BM - 1) / C::BM;
     hipLaunchKernelGGL((fwd_kernel_bf16<D, CAUSAL, SPARSE>), dim3(nqblk * BH), dim3(64 * fwd_bf16_waves<SPARSE>()), 0,
                        st, (const bf16*)Q,
-                       (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk, fabsf(scale) * kLog2e,
+                       (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk,
+                       fmaxf(fabsf(scale) * kLog2e, FLT_MIN),       // scale 0: -inf * c stays -inf
                        (int)(scale < 0.f), bmask, mhead, tune_lookup(kTuneFwdBf16, D, CAUSAL, N).slots);
     return hipGetLastError();
 }
