@@ -831,17 +831,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sK, 32 * kt, s), qf[s], sacc[kt], 0, 0, 0);
                 pacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sV, 32 * kt, s), gf[s], pacc[kt], 0, 0, 0);
             }
-        // key kv0 + 32 kt + 8 (r/4) + 4 h + r%4 of this lane's query
-        const bool need_mask = CAUSAL && (kv0 + C::BN - 1 > q0w);
         bf16x8 sb[C::NKT][2];
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(sacc[kt][r], c2, nlse));
-                if (need_mask && kv0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3) > myq) p = 0.f;
-                sb[kt][r >> 3][r & 7] = to_bf16(p * (pacc[kt][r] - dq_d));
-            }
+            for (int r = 0; r < 16; ++r)
+                sb[kt][r >> 3][r & 7] = to_bf16(fast_exp2(fmaf(sacc[kt][r], c2, nlse)) * (pacc[kt][r] - dq_d));
+        // key kv0 + 4 h + cr (cr = 32 kt + 8 (r/4) + r%4) of this lane's query: on tiles that cross
+        // the wave's diagonal, dS = 0 where the key follows the query (cr above the bound); this
+        // also replaces whatever a masked key's exponential gave
+        if (CAUSAL && (kv0 + C::BN - 1 > q0w)) {
+            const int bound = myq - kv0 - 4 * h;
+#pragma unroll
+            for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {           // packed pair: elements r = 2w, 2w + 1
+                    const int r = 2 * w;
+                    u32x4 v = __builtin_bit_cast(u32x4, sb[kt][r >> 3]);
+                    uint32_t x = v[(r & 7) >> 1];
+                    if (32 * kt + 8 * (r >> 2) + (r & 3) > bound) x &= 0xFFFF0000u;
+                    if (32 * kt + 8 * (r >> 2) + (r & 3) + 1 > bound) x &= 0x0000FFFFu;
+                    v[(r & 7) >> 1] = x;
+                    sb[kt][r >> 3] = __builtin_bit_cast(bf16x8, v);
+                }
+        }
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
