@@ -824,13 +824,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
         for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) { sacc[kt][r] = 0.f; pacc[kt][r] = 0.f; }
+        {
+            // S^T and dP^T products, f = 4 s + 2 kt + (0: K row -> S^T, 1: V row -> dP^T); the K and V
+            // fragments are read PF products ahead through a small ring (sched_barrier keeps the order)
+            constexpr int NF = 4 * C::NKS, PF = 4;
+            static_assert(C::NKT == 2, "two 32-key halves per tile");
+            auto frag = [&](int f) __attribute__((always_inline)) {
+                return tl.row((f & 1) ? sV : sK, 32 * ((f >> 1) & 1), f >> 2);
+            };
+            bf16x8 ring[PF];
 #pragma unroll
-        for (int s = 0; s < C::NKS; ++s)
+            for (int f = 0; f < PF; ++f) ring[f] = frag(f);
 #pragma unroll
-            for (int kt = 0; kt < C::NKT; ++kt) {
-                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sK, 32 * kt, s), qf[s], sacc[kt], 0, 0, 0);
-                pacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.row(sV, 32 * kt, s), gf[s], pacc[kt], 0, 0, 0);
+            for (int f = 0; f < NF; ++f) {
+                const bf16x8 a = ring[f % PF];
+                if (f + PF < NF) ring[f % PF] = frag(f + PF);
+                const int s = f >> 2, kt = (f >> 1) & 1;
+                if (f & 1) pacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[s], pacc[kt], 0, 0, 0);
+                else sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
         bf16x8 sb[C::NKT][2];
 #pragma unroll
         for (int kt = 0; kt < C::NKT; ++kt)
