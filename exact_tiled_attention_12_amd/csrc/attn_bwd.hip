@@ -869,14 +869,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
                     sb[kt][r >> 3] = __builtin_bit_cast(bf16x8, v);
                 }
         }
+        {
+            // dQ^T += K^T dS^T, m = (2 kt + s2) NDT + dt; the K^T fragments (transpose reads) go PF
+            // products ahead through a ring
+            constexpr int NM = 2 * C::NKT * C::NDT, PF = 2;
+            auto tfrag = [&](int m) __attribute__((always_inline)) {
+                return tl.tr(sK, 16 * (m / C::NDT), m % C::NDT);
+            };
+            bf16x8 ring[PF];
 #pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt)
+            for (int m = 0; m < PF; ++m) ring[m] = tfrag(m);
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt)
-                    dqacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tl.tr(sK, 32 * kt + 16 * s2, dt), sb[kt][s2],
-                                                                        dqacc[dt], 0, 0, 0);
+            for (int m = 0; m < NM; ++m) {
+                const bf16x8 a = ring[m % PF];
+                if (m + PF < NM) ring[m % PF] = tfrag(m + PF);
+                const int ks = m / C::NDT;             // 2 kt + s2
+                dqacc[m % C::NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[ks >> 1][ks & 1], dqacc[m % C::NDT],
+                                                                            0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
     };
 
     if constexpr (!SPARSE) {
