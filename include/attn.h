@@ -94,8 +94,11 @@ attn_status attn_bwd_dq(const void* Q, const void* K, const void* V, const void*
 /* Backward, query side with the preprocess folded in: like attn_bwd_dq, but D
  * is an output.  Each workgroup computes D_i = sum_k dO_ik O_ik (fp32) for its
  * own query rows from O and the dO rows it loads anyway, uses it for dS, and
- * writes it to D [B,H,N] for an attn_bwd_dkdv call that follows.  O: dtype dt
- * (ATTN_BF16 only, else ATTN_EUNSUPPORTED), 16-byte aligned.  This is the
+ * writes it to D for an attn_bwd_dkdv call that follows (same stream, or
+ * ordered after this call).  O: device, dtype dt, [B,H,N,d] like Q, 16-byte
+ * aligned.  D: device fp32 [B,H,N], 16-byte aligned, fully overwritten.  dQ as
+ * in attn_bwd_dq.  dt must be ATTN_BF16 (else ATTN_EUNSUPPORTED); a null or
+ * misaligned pointer gives ATTN_EINVAL and nothing is launched.  This is the
  * order attn_bwd takes for bf16 inputs: one pass over O and dO fewer than
  * attn_bwd_preprocess + attn_bwd_dq. */
 attn_status attn_bwd_dq_d(const void* Q, const void* K, const void* V, const void* O,
