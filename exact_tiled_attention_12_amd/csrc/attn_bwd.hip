@@ -817,21 +817,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
         dma_rows<D, RB, true>(make_rsrc(Vh + (size_t)kv0 * D, bytes), sV, wave * (C::BN / 4), C::BN / 4, lane);
     };
 
+    // One key tile, ordered so that each wave's VALU work overlaps its own MFMAs:
+    //   S^T = K Q^T;  dP^T = V dO^T while P^T = exp2(S^T c2 - LSE log2 e) is computed (in place);
+    //   dS^T of keys 0-31;  dQ^T += K^T dS^T for keys 0-31 while dS^T of keys 32-63 is computed;
+    //   dQ^T += K^T dS^T for keys 32-63.  Fragments go PF products ahead through small rings.
     auto tile_body = [&](int j, const char* sK, const char* sV) {
+        static_assert(C::NKT == 2, "two 32-key halves per tile");
         const int kv0 = j * C::BN;
+        const bool diag = CAUSAL && (kv0 + C::BN - 1 > q0w);
+        const int bound = myq - kv0 - 4 * h;            // key kv0 + 4 h + cr follows the query when cr > bound
         f32x16 sacc[C::NKT], pacc[C::NKT];
-#pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { sacc[kt][r] = 0.f; pacc[kt][r] = 0.f; }
+        constexpr int NF = 2 * C::NKS, PF = 4;          // f = 2 s + kt
         {
-            // S^T and dP^T products, f = 4 s + 2 kt + (0: K row -> S^T, 1: V row -> dP^T); the K and V
-            // fragments are read PF products ahead through a small ring (sched_barrier keeps the order)
-            constexpr int NF = 4 * C::NKS, PF = 4;
-            static_assert(C::NKT == 2, "two 32-key halves per tile");
-            auto frag = [&](int f) __attribute__((always_inline)) {
-                return tl.row((f & 1) ? sV : sK, 32 * ((f >> 1) & 1), f >> 2);
-            };
+            auto frag = [&](int f) __attribute__((always_inline)) { return tl.row(sK, 32 * (f & 1), f >> 1); };
             bf16x8 ring[PF];
 #pragma unroll
             for (int f = 0; f < PF; ++f) ring[f] = frag(f);
@@ -839,53 +837,72 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
             for (int f = 0; f < NF; ++f) {
                 const bf16x8 a = ring[f % PF];
                 if (f + PF < NF) ring[f % PF] = frag(f + PF);
-                const int s = f >> 2, kt = (f >> 1) & 1;
-                if (f & 1) pacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[s], pacc[kt], 0, 0, 0);
-                else sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+                sacc[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[f >> 1], f < 2 ? f32x16{} : sacc[f & 1],
+                                                                      0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        bf16x8 sb[C::NKT][2];
-#pragma unroll
-        for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sb[kt][r >> 3][r & 7] = to_bf16(fast_exp2(fmaf(sacc[kt][r], c2, nlse)) * (pacc[kt][r] - dq_d));
-        // key kv0 + 4 h + cr (cr = 32 kt + 8 (r/4) + r%4) of this lane's query: on tiles that cross
-        // the wave's diagonal, dS = 0 where the key follows the query (cr above the bound); this
-        // also replaces whatever a masked key's exponential gave
-        if (CAUSAL && (kv0 + C::BN - 1 > q0w)) {
-            const int bound = myq - kv0 - 4 * h;
-#pragma unroll
-            for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {           // packed pair: elements r = 2w, 2w + 1
-                    const int r = 2 * w;
-                    u32x4 v = __builtin_bit_cast(u32x4, sb[kt][r >> 3]);
-                    uint32_t x = v[(r & 7) >> 1];
-                    if (32 * kt + 8 * (r >> 2) + (r & 3) > bound) x &= 0xFFFF0000u;
-                    if (32 * kt + 8 * (r >> 2) + (r & 3) + 1 > bound) x &= 0x0000FFFFu;
-                    v[(r & 7) >> 1] = x;
-                    sb[kt][r >> 3] = __builtin_bit_cast(bf16x8, v);
-                }
-        }
         {
-            // dQ^T += K^T dS^T, m = (2 kt + s2) NDT + dt; the K^T fragments (transpose reads) go PF
-            // products ahead through a ring
-            constexpr int NM = 2 * C::NKT * C::NDT, PF = 2;
+            auto frag = [&](int f) __attribute__((always_inline)) { return tl.row(sV, 32 * (f & 1), f >> 1); };
+            bf16x8 ring[PF];
+#pragma unroll
+            for (int f = 0; f < PF; ++f) ring[f] = frag(f);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                const bf16x8 a = ring[f % PF];
+                if (f + PF < NF) ring[f % PF] = frag(f + PF);
+                pacc[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[f >> 1], f < 2 ? f32x16{} : pacc[f & 1],
+                                                                      0, 0, 0);
+                // P of score elements [32 f / NF, 32 (f + 1) / NF), element e = 16 kt + r
+#pragma unroll
+                for (int e = 32 * f / NF; e < 32 * (f + 1) / NF; ++e)
+                    sacc[e >> 4][e & 15] = fast_exp2(fmaf(sacc[e >> 4][e & 15], c2, nlse));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // dS^T = P^T o (dP^T - D) in bf16; on tiles that cross the wave's diagonal, 0 where the key
+        // follows the query (this also replaces whatever a masked key's exponential gave)
+        bf16x8 sb[C::NKT][2];
+        auto ds_elem = [&](int kt, int r) __attribute__((always_inline)) {
+            sb[kt][r >> 3][r & 7] = to_bf16(sacc[kt][r] * (pacc[kt][r] - dq_d));
+        };
+        auto ds_mask = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {               // packed pair: elements r = 2w, 2w + 1
+                const int r = 2 * w;
+                u32x4 v = __builtin_bit_cast(u32x4, sb[kt][r >> 3]);
+                uint32_t x = v[(r & 7) >> 1];
+                if (32 * kt + 8 * (r >> 2) + (r & 3) > bound) x &= 0xFFFF0000u;
+                if (32 * kt + 8 * (r >> 2) + (r & 3) + 1 > bound) x &= 0x0000FFFFu;
+                v[(r & 7) >> 1] = x;
+                sb[kt][r >> 3] = __builtin_bit_cast(bf16x8, v);
+            }
+        };
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds_elem(0, r);
+        if (diag) ds_mask(0);
+        {
+            // dQ^T += K^T dS^T, m = (2 kt + s2) NDT + dt; the K^T fragments (transpose reads) go PF2
+            // products ahead through a ring; dS^T of keys 32-63 between the products of keys 0-31
+            constexpr int NM = 2 * C::NKT * C::NDT, NM0 = 2 * C::NDT, PF2 = 2;
             auto tfrag = [&](int m) __attribute__((always_inline)) {
                 return tl.tr(sK, 16 * (m / C::NDT), m % C::NDT);
             };
-            bf16x8 ring[PF];
+            bf16x8 ring[PF2];
 #pragma unroll
-            for (int m = 0; m < PF; ++m) ring[m] = tfrag(m);
+            for (int m = 0; m < PF2; ++m) ring[m] = tfrag(m);
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                const bf16x8 a = ring[m % PF];
-                if (m + PF < NM) ring[m % PF] = tfrag(m + PF);
+                if (m == NM0 && diag) ds_mask(1);
+                const bf16x8 a = ring[m % PF2];
+                if (m + PF2 < NM) ring[m % PF2] = tfrag(m + PF2);
                 const int ks = m / C::NDT;             // 2 kt + s2
                 dqacc[m % C::NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, sb[ks >> 1][ks & 1], dqacc[m % C::NDT],
                                                                             0, 0, 0);
+                if (m < NM0) {
+#pragma unroll
+                    for (int r = 16 * m / NM0; r < 16 * (m + 1) / NM0; ++r) ds_elem(1, r);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
