@@ -58,7 +58,7 @@ def lib():
         L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
         L.attn_bwd_dq_d.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp]
         L.attn_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp]
-        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.attn_bwd_workspace_bytes.restype = sz
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, i, vp, sz, vp]
         L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, vp]
@@ -111,6 +111,34 @@ def _check_inputs(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(t, name, shape, dtype):
+    """Raises unless tensor t (an argument called `name`) has exactly this shape and dtype: the
+    C ABI takes raw pointers and cannot tell a wrong-sized buffer from a right one."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _expect_like_q(q, **ts):
+    for name, t in ts.items():
+        _expect(t, name, q.shape, q.dtype)
+
+
+def _expect_rows(q, **ts):
+    """fp32 [B, H, N] row statistics (LSE, D)."""
+    for name, t in ts.items():
+        _expect(t, name, q.shape[:-1], torch.float32)
+
+
+def _workspace(workspace, need, dev):
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold at least {need} bytes")
+    return workspace
+
+
 def _call(name, *args):
     st = getattr(lib(), name)(*args)
     if st != ATTN_OK:
@@ -120,43 +148,60 @@ def _call(name, *args):
 def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """O = softmax(scale Q K^T) V and LSE.  Returns (O, LSE)."""
     B, H, N, d = _shape(q)
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
-    _check_inputs(q, k, v)
+    _dt(q)
+    _expect_like_q(q, k=k, v=v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_inputs(q, o, l)
+    _expect_like_q(q, out=o)
+    _expect_rows(q, lse=l)
+    _check_inputs(q, k, v, o, l)
     _call("attn_fwd", _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, float(scale), int(bool(causal)),
           _ptr(o), _ptr(l), _stream(q, stream))
     return o, l
 
 
-def attn_bwd_workspace_bytes(B, H, N, d):
-    return int(lib().attn_bwd_workspace_bytes(B, H, N, d))
+def attn_bwd_workspace_bytes(B, H, N, d, grad_dtype=torch.float32):
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d, _gdt(grad_dtype)))
+
+
+def _gdt(grad_dtype):
+    if grad_dtype == torch.bfloat16:
+        return ATTN_BF16
+    if grad_dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"gradients must be float32 or bfloat16, not {grad_dtype}")
 
 
 def attn_bwd_preprocess(o, do, D=None, stream=None):
     """D = rowsum(dO o O), fp32 [B, H, N]."""
     B, H, N, d = _shape(o)
-    _check_inputs(o, do)
+    _dt(o)
+    _expect_like_q(o, do=do)
     D = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if D is None else D
+    _expect_rows(o, D=D)
+    _check_inputs(o, do, D)
     _call("attn_bwd_preprocess", _ptr(o), _ptr(do), _dt(o), B, H, N, d, _ptr(D), _stream(o, stream))
     return D
 
 
-def _grad(t, q):
-    B, H, N, d = _shape(q)
-    return torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) if t is None else t
+def _grad(t, q, dtype=torch.float32, name="gradient"):
+    """A caller's gradient buffer (checked: [B, H, N, d] of `dtype`), or a new one."""
+    if t is None:
+        return torch.empty(q.shape, dtype=dtype, device=q.device)
+    _expect(t, name, q.shape, dtype)
+    return t
 
 
 def attn_bwd_dkdv(q, k, v, do, lse, D, scale=None, causal=False, dk=None, dv=None, stream=None):
     """dK, dV (fp32, written once).  bf16 inputs only."""
     B, H, N, d = _shape(q)
-    _check_inputs(q, k, v, do, lse, D)
+    _expect_like_q(q, k=k, v=v, do=do)
+    _expect_rows(q, lse=lse, D=D)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     dk, dv = _grad(dk, q), _grad(dv, q)
+    _check_inputs(q, k, v, do, lse, D, dk, dv)
     _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(dk), _ptr(dv), _stream(q, stream))
     return dk, dv
@@ -165,9 +210,11 @@ def attn_bwd_dkdv(q, k, v, do, lse, D, scale=None, causal=False, dk=None, dv=Non
 def attn_bwd_dq(q, k, v, do, lse, D, scale=None, causal=False, dq=None, stream=None):
     """dQ (fp32, written once).  bf16 inputs only."""
     B, H, N, d = _shape(q)
-    _check_inputs(q, k, v, do, lse, D)
+    _expect_like_q(q, k=k, v=v, do=do)
+    _expect_rows(q, lse=lse, D=D)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     dq = _grad(dq, q)
+    _check_inputs(q, k, v, do, lse, D, dq)
     _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(dq), _stream(q, stream))
     return dq
@@ -177,15 +224,13 @@ def attn_bwd_dq_d(q, k, v, o, do, lse, D=None, scale=None, causal=False, dq=None
     """(dQ, D): dQ (fp32, written once) with the preprocess folded in: D = rowsum(dO o O) is
     computed per query row, used, and returned for an attn_bwd_dkdv call.  bf16 inputs only."""
     B, H, N, d = _shape(q)
-    if o.shape != q.shape or o.dtype != q.dtype:
-        raise ValueError("o must match q in shape and dtype")
+    _expect_like_q(q, k=k, v=v, o=o, do=do)
     if D is None:
         D = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif D.shape != (B, H, N) or D.dtype != torch.float32:
-        raise ValueError("D must be fp32 [B, H, N]")
-    _check_inputs(q, k, v, o, do, lse, D)
+    _expect_rows(q, lse=lse, D=D)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     dq = _grad(dq, q)
+    _check_inputs(q, k, v, o, do, lse, D, dq)
     _call("attn_bwd_dq_d", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(D), _ptr(dq), _stream(q, stream))
     return dq, D
@@ -194,9 +239,12 @@ def attn_bwd_dq_d(q, k, v, o, do, lse, D=None, scale=None, causal=False, dq=None
 def attn_bwd_main(q, k, v, do, lse, D, scale=None, causal=False, dq=None, dk=None, dv=None, stream=None):
     """dQ, dK, dV (fp32, written once) given D from attn_bwd_preprocess."""
     B, H, N, d = _shape(q)
-    _check_inputs(q, k, v, do, lse, D)
+    _dt(q)
+    _expect_like_q(q, k=k, v=v, do=do)
+    _expect_rows(q, lse=lse, D=D)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     dq, dk, dv = _grad(dq, q), _grad(dk, q), _grad(dv, q)
+    _check_inputs(q, k, v, do, lse, D, dq, dk, dv)
     _call("attn_bwd_main", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(D), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _stream(q, stream))
     return dq, dk, dv
@@ -206,15 +254,15 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, grad_dtype=torch.flo
              dq=None, dk=None, dv=None, stream=None):
     """Full backward.  Returns (dQ, dK, dV) in grad_dtype."""
     B, H, N, d = _shape(q)
-    _check_inputs(q, k, v, o, do, lse)
+    _dt(q)
+    _expect_like_q(q, k=k, v=v, o=o, do=do)
+    _expect_rows(q, lse=lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    gdt = ATTN_BF16 if grad_dtype == torch.bfloat16 else ATTN_F32
-    need = attn_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    mk = lambda t: torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) if t is None else t
-    dq, dk, dv = mk(dq), mk(dk), mk(dv)
+    gdt = _gdt(grad_dtype)
+    workspace = _workspace(workspace, attn_bwd_workspace_bytes(B, H, N, d, grad_dtype), q.device)
+    dq, dk, dv = (_grad(t, q, grad_dtype, n) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    _check_inputs(q, k, v, o, do, lse, dq, dk, dv, workspace)
     _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), gdt, _ptr(workspace),
           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q, stream))
@@ -233,7 +281,6 @@ def _block_mask(mask, q):
         heads = B * H
     else:
         raise ValueError(f"block mask must be [{T}, {T}] or [{B}, {H}, {T}, {T}]")
-    _check_inputs(q, mask)
     return mask, heads
 
 
@@ -241,15 +288,16 @@ def attn_fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False, out=None
     """Forward restricted to the kept blocks of block_mask (uint8 [T, T] or [B, H, T, T],
     T = ceil(N / 128)).  Rows that keep no key get O = 0 and LSE = -inf.  Returns (O, LSE)."""
     B, H, N, d = _shape(q)
-    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
-    _check_inputs(q, k, v)
+    _dt(q)
+    _expect_like_q(q, k=k, v=v)
     m, heads = _block_mask(block_mask, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_inputs(q, o, l)
+    _expect_like_q(q, out=o)
+    _expect_rows(q, lse=l)
+    _check_inputs(q, k, v, o, l, m)
     _call("attn_fwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, float(scale),
           int(bool(causal)), _ptr(m), heads, _ptr(o), _ptr(l), _stream(q, stream))
     return o, l
@@ -259,16 +307,16 @@ def attn_bwd_blocksparse(q, k, v, o, do, lse, block_mask, scale=None, causal=Fal
                          workspace=None, dq=None, dk=None, dv=None, stream=None):
     """Backward of attn_fwd_blocksparse (same mask, scale and causal flag).  Returns (dQ, dK, dV)."""
     B, H, N, d = _shape(q)
-    _check_inputs(q, k, v, o, do, lse)
+    _dt(q)
+    _expect_like_q(q, k=k, v=v, o=o, do=do)
+    _expect_rows(q, lse=lse)
     m, heads = _block_mask(block_mask, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    gdt = ATTN_BF16 if grad_dtype == torch.bfloat16 else ATTN_F32
-    need = attn_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    mk = lambda t: torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) if t is None else t
-    dq, dk, dv = mk(dq), mk(dk), mk(dv)
+    gdt = _gdt(grad_dtype)
+    workspace = _workspace(workspace, attn_bwd_workspace_bytes(B, H, N, d, grad_dtype), q.device)
+    dq, dk, dv = (_grad(t, q, grad_dtype, n) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    _check_inputs(q, k, v, o, do, lse, dq, dk, dv, workspace, m)
     _call("attn_bwd_blocksparse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(m), heads, _ptr(dq), _ptr(dk), _ptr(dv), gdt, _ptr(workspace),
           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q, stream))
@@ -283,12 +331,13 @@ def attn_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal
     for t in (q8, k8, v8):
         if t.dtype != torch.float8_e4m3fn or t.shape != q8.shape:
             raise ValueError("q8, k8, v8 must be float8_e4m3fn tensors of one shape")
-    _check_inputs(q8, k8, v8)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
-    _check_inputs(q8, o, l)
+    _expect(o, "out", q8.shape, torch.bfloat16)
+    _expect_rows(q8, lse=l)
+    _check_inputs(q8, k8, v8, o, l)
     _call("attn_fwd_fp8", _ptr(q8), _ptr(k8), _ptr(v8), float(q_descale), float(k_descale), float(v_descale),
           B, H, N, d, float(scale), int(bool(causal)), _ptr(o), _ptr(l), _stream(q8, stream))
     return o, l

@@ -16,11 +16,13 @@ bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr
 attn_status check_shape(int B, int H, int N, int d)
 {
     if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_EINVAL;
-    const long long total = (long long)B * H * N * d;
-    if (total >= (1LL << 31)) return ATTN_EINVAL;
-    // one head's fp32 rows must stay below 2 GiB: the kernels address a head
-    // with 32-bit byte offsets and use 2^31 as their out-of-range offset
+    // one head's fp32 rows must stay below 2 GiB: the kernels address inside a head
+    // with 32-bit byte offsets (heads themselves with 64-bit ones) and use 2^31 as
+    // their out-of-range offset
     if ((long long)N * d * 4 >= (1LL << 31)) return ATTN_EINVAL;
+    // the largest grid (one 512-thread workgroup per 128 rows of every head) must
+    // stay below 2^32 work-items, the dispatch packet's limit
+    if ((long long)B * H * ((N + 127) / 128) >= (1LL << 23)) return ATTN_EINVAL;
     if (d != 64 && d != 80 && d != 128) return ATTN_EUNSUPPORTED;
     return ATTN_OK;
 }
@@ -139,9 +141,12 @@ attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const voi
                                         dQ, false, nullptr, 0, st));
 }
 
-size_t attn_bwd_workspace_bytes(int B, int H, int N, int d)
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype grad_dt)
 {
-    if (check_shape(B, H, N, d) == ATTN_EINVAL) return 0;
+    if (check_shape(B, H, N, d) == ATTN_EINVAL || !dtype_ok(grad_dt)) return 0;
+    // D only: every gradient is written once in its own dtype (dQ by the query-side
+    // kernel, or for fp32 inputs accumulated in place in the fp32 dQ), so no fp32
+    // staging of bf16 gradients is needed
     return round256((size_t)B * H * N * sizeof(float));
 }
 
@@ -154,7 +159,7 @@ static attn_status bwd_all(const void* Q, const void* K, const void* V, const vo
     if (s != ATTN_OK) return s;
     if (!dtype_ok(grad_dt)) return ATTN_EINVAL;
     if (!aligned16(O) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV)) return ATTN_EINVAL;
-    if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_EINVAL;
+    if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, grad_dt)) return ATTN_EINVAL;
     if (dt == ATTN_F32 && grad_dt == ATTN_BF16) return ATTN_EUNSUPPORTED;
 
     hipStream_t st = (hipStream_t)stream;

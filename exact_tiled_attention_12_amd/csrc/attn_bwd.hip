@@ -34,42 +34,53 @@ namespace attn {
 
 // ----------------------------------------------------------------------------
 // Preprocess: D_i = sum_k dO_ik O_ik (fp32).  Memory bound: 8 lanes per row,
-// 32 rows per 256-thread block, 16-byte loads.
+// 32 rows per 256-thread block, 16-byte loads; a grid-stride loop over row
+// groups, so the grid stays small for any number of rows.
 // ----------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                       float* __restrict__ Dout, long rows)
 {
     constexpr int CH = Mma<T>::CH, CPR = D / CH, LPR = 8;
-    const long row = (long)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
     const int u = threadIdx.x % LPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const T* o = O + row * D;
-        const T* g = dO + row * D;
-        for (int cidx = u; cidx < CPR; cidx += LPR) {
-            const u32x4 a = ld16(o + cidx * CH), b = ld16(g + cidx * CH);
-            if constexpr (sizeof(T) == 2) {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
+    for (long row = (long)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR); row - (threadIdx.x / LPR) < rows;
+         row += (long)gridDim.x * (256 / LPR)) {
+        float acc = 0.f;
+        if (row < rows) {
+            const T* o = O + row * D;
+            const T* g = dO + row * D;
+            for (int cidx = u; cidx < CPR; cidx += LPR) {
+                const u32x4 a = ld16(o + cidx * CH), b = ld16(g + cidx * CH);
+                if constexpr (sizeof(T) == 2) {
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf((float)av[e], (float)bv[e], acc);
-            } else {
-                const f32x4 av = __builtin_bit_cast(f32x4, a), bv = __builtin_bit_cast(f32x4, b);
+                    for (int e = 0; e < 8; ++e) acc = fmaf((float)av[e], (float)bv[e], acc);
+                } else {
+                    const f32x4 av = __builtin_bit_cast(f32x4, a), bv = __builtin_bit_cast(f32x4, b);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc = fmaf(av[e], bv[e], acc);
+                    for (int e = 0; e < 4; ++e) acc = fmaf(av[e], bv[e], acc);
+                }
             }
         }
-    }
+        // every lane of the wave takes part in the shuffles (the loop condition is uniform per block)
 #pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && u == 0) Dout[row] = acc;
+        for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (row < rows && u == 0) Dout[row] = acc;
+    }
 }
 
-// Zero fill (a kernel rather than a memset, so callers may capture it in a graph).
+// Zero fill (a kernel rather than a memset, so callers may capture it in a graph); grid-stride.
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, long n4)
 {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i < n4) st16(p + 4 * i, zero4());
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) st16(p + 4 * i, zero4());
+}
+
+// Blocks of an elementwise grid-stride launch: enough to fill the GPU several times over,
+// never more than the work needs.
+static inline unsigned stride_grid(long work_blocks)
+{
+    const long cap = 256L * 64;
+    return (unsigned)(work_blocks < 1 ? 1 : work_blocks < cap ? work_blocks : cap);
 }
 
 // ----------------------------------------------------------------------------
@@ -824,8 +835,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
     auto tile_body = [&](int j, const char* sK, const char* sV) {
         static_assert(C::NKT == 2, "two 32-key halves per tile");
         const int kv0 = j * C::BN;
-        const bool diag = CAUSAL && (kv0 + C::BN - 1 > q0w);
-        const int bound = myq - kv0 - 4 * h;            // key kv0 + 4 h + cr follows the query when cr > bound
+        // key kv0 + 4 h + cr is masked (follows the query, or lies past N) when cr > bound; only
+        // tiles that cross the wave's diagonal or N need it.  A key past N reads as a zero row,
+        // whose P = exp(-LSE) can overflow when every score of the row is very negative, so the
+        // ragged tile is masked under both mask settings.
+        const bool diag = (CAUSAL && kv0 + C::BN - 1 > q0w) || (kv0 + C::BN > N);
+        const int bound = (CAUSAL ? min(myq, N - 1) : N - 1) - kv0 - 4 * h;
         f32x16 sacc[C::NKT], pacc[C::NKT];
         constexpr int NF = 2 * C::NKS, PF = 4;          // f = 2 s + kt
         {
@@ -860,8 +875,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // dS^T = P^T o (dP^T - D) in bf16; on tiles that cross the wave's diagonal, 0 where the key
-        // follows the query (this also replaces whatever a masked key's exponential gave)
+        // dS^T = P^T o (dP^T - D) in bf16; on masked tiles, 0 where the key follows the query or
+        // lies past N (this also replaces whatever a masked key's exponential gave, inf included)
         bf16x8 sb[C::NKT][2];
         auto ds_elem = [&](int kt, int r) __attribute__((always_inline)) {
             sb[kt][r >> 3][r & 7] = to_bf16(sacc[kt][r] * (pacc[kt][r] - dq_d));
@@ -973,18 +988,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(const bf16* __restrict__ Q
     }
 }
 
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, long n4)
-{
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i < n4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * i);
-        bf16x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = to_bf16(v[e]);
-        *reinterpret_cast<bf16x4*>(dst + 4 * i) = o;
-    }
-}
-
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
@@ -992,7 +995,7 @@ template <typename T, int D>
 static hipError_t pre_t(const void* O, const void* dO, int BH, int N, float* Dd, hipStream_t st)
 {
     const long rows = (long)BH * N;
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, st, (const T*)O,
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(stride_grid((rows + 31) / 32)), dim3(256), 0, st, (const T*)O,
                        (const T*)dO, Dd, rows);
     return hipGetLastError();
 }
@@ -1096,7 +1099,7 @@ static hipError_t f32_t(const void* Q, const void* K, const void* V, const void*
 {
     using C = BwdCfg<float, D>;
     const long n4 = (long)BH * N * D / 4;
-    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dQacc, n4);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(stride_grid((n4 + 255) / 256)), dim3(256), 0, st, dQacc, n4);
     const int nkblk = (N + C::BN - 1) / C::BN;
     const int slots = tune_lookup(kTuneBwdF32, D, CAUSAL, N).slots;
     if (bmask)
@@ -1122,15 +1125,6 @@ hipError_t launch_bwd_f32(const void* Q, const void* K, const void* V, const voi
     }
 #undef ATTN_F32_ARGS
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_f32_to_bf16(const float* src, void* dst, long n, hipStream_t st)
-{
-    const long n4 = n / 4;
-    if (n4 > 0)
-        hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, src,
-                           (bf16*)dst, n4);
-    return hipGetLastError();
 }
 
 }  // namespace attn

@@ -300,7 +300,7 @@ inline hipError_t device_cu_count(int* n)
 // Workgroup index -> logical index so that consecutive logical indices (the
 // blocks of one head) run on the same XCD and share its L2.  Hardware hands
 // workgroups to the 8 XCDs round-robin.
-__device__ __forceinline__ int xcd_remap(int bid, int nb) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
     if ((nb & 7) != 0) return bid;
     return (bid & 7) * (nb >> 3) + (bid >> 3);
 }
@@ -316,7 +316,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 // first (key-side kernels).  Without 8 | BH the whole GPU is one group sequence.
 // (`slots` comes from the launch-parameter table of attn_tuning.h.)
 template <bool CAUSAL, bool HEAVY_LAST>
-__device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int SLOTS, int& head, int& blk)
+__host__ __device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int SLOTS, int& head, int& blk)
 {
     if constexpr (!CAUSAL) {
         const int b = xcd_remap(bid, nb);
@@ -329,9 +329,9 @@ __device__ __forceinline__ void block_coords(int bid, int nb, int nblk, int SLOT
         const int k = split ? bid >> 3 : bid;           // position in its sequence
         const int x = split ? (bid & 7) : 0;
         const int slots = split ? SLOTS : 8 * SLOTS;
-        const int G = min(hx, (slots + nblk - 1) / nblk);
+        const int G = hx < (slots + nblk - 1) / nblk ? hx : (slots + nblk - 1) / nblk;
         const int g = k / (G * nblk);
-        const int gh = min(G, hx - g * G);              // heads in this group
+        const int gh = G < hx - g * G ? G : hx - g * G; // heads in this group
         const int kk = k - g * G * nblk;
         const int rank = kk / gh;
         head = x * hx + g * G + (kk - rank * gh);
@@ -354,7 +354,7 @@ __host__ __device__ __forceinline__ bool items_split(int nitems, int nblk)
 struct ItemWalk {
     int xcd, pc, P, KX;
     bool split;
-    __device__ __forceinline__ void init(int bid, int nwg, int nitems, bool split_)
+    __host__ __device__ __forceinline__ void init(int bid, int nwg, int nitems, bool split_)
     {
         split = split_;
         xcd = split ? (bid & 7) : 0;
@@ -363,7 +363,7 @@ struct ItemWalk {
         KX = split ? (nitems >> 3) : nitems;
     }
     // the item of step t of this workgroup, or -1 once its share is done
-    __device__ __forceinline__ int item(int t) const
+    __host__ __device__ __forceinline__ int item(int t) const
     {
         const int pos = (t & 1) ? (t + 1) * P - 1 - pc : t * P + pc;
         if (pos >= KX) return -1;

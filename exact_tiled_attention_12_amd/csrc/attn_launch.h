@@ -39,6 +39,4 @@ hipError_t launch_fwd_fp8(const void* Q, const void* K, const void* V, float q_d
                           float v_descale, void* O, float* LSE, int BH, int N, int d, float scale, int causal,
                           hipStream_t st);
 
-hipError_t launch_f32_to_bf16(const float* src, void* dst, long n, hipStream_t st);
-
 }  // namespace attn

@@ -18,7 +18,9 @@
  *   - Q, K, V, O, dO, dQ, dK, dV are device pointers to contiguous row-major
  *     [B, H, N, d] arrays (d fastest).  LSE and D are device fp32 [B, H, N].
  *   - d must be 64, 80 or 128 (else ATTN_EUNSUPPORTED).  B, H, N >= 1,
- *     B*H*N*d < 2^31 and N*d < 2^29 (else ATTN_EINVAL).  Q, K, V have the same N.
+ *     N*d < 2^29 (one head below 2 GiB of fp32) and B*H*ceil(N/128) < 2^23 (the
+ *     launch grids' limit) (else ATTN_EINVAL).  The total B*H*N*d is not limited
+ *     otherwise: heads are addressed with 64-bit offsets.  Q, K, V have the same N.
  *   - scale must be finite (else ATTN_EINVAL); its sign is arbitrary.
  *   - Every pointer must be non-NULL and 16-byte aligned (else ATTN_EINVAL).
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).
@@ -114,9 +116,11 @@ attn_status attn_bwd_main(const void* Q, const void* K, const void* V, const voi
                           int B, int H, int N, int d, float scale, int causal,
                           float* dQ, float* dK, float* dV, void* stream);
 
-/* Bytes of device workspace attn_bwd needs: D (B*H*N fp32) rounded up to 256
- * bytes.  Returns 0 for invalid sizes. */
-size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+/* Bytes of device workspace attn_bwd (and attn_bwd_blocksparse) needs for
+ * gradients of dtype grad_dt: D (B*H*N fp32) rounded up to 256 bytes, the same
+ * for both gradient dtypes (every gradient is written once in its own dtype, so
+ * no fp32 staging buffer exists).  Returns 0 for invalid sizes or dtypes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d, attn_dtype grad_dt);
 
 /* Full backward.  bf16 inputs: attn_bwd_dq_d (dQ, and D into the workspace),
  * then attn_bwd_dkdv.  fp32 inputs: attn_bwd_preprocess + attn_bwd_main.  The
@@ -124,7 +128,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
  * `dt`; LSE from attn_fwd with the same scale and causal flag.  dQ, dK, dV:
  * outputs of dtype grad_dt (ATTN_BF16 gradients need bf16 inputs, else
  * ATTN_EUNSUPPORTED).  workspace: device, 16-byte aligned, at least
- * attn_bwd_workspace_bytes(B, H, N, d) bytes (else ATTN_EINVAL). */
+ * attn_bwd_workspace_bytes(B, H, N, d, grad_dt) bytes (else ATTN_EINVAL). */
 attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                      const void* dO, const float* LSE, attn_dtype dt,
                      int B, int H, int N, int d, float scale, int causal,

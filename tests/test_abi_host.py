@@ -52,7 +52,8 @@ def fwd(*, dt=1, B=1, H=1, N=16, d=64, scale=0.125, causal=0, q=P, o=P, lse=P):
     (dict(q=MIS), attn.ATTN_EINVAL),
     (dict(o=NUL), attn.ATTN_EINVAL),
     (dict(lse=MIS), attn.ATTN_EINVAL),
-    (dict(B=64, H=64, N=4096, d=128), attn.ATTN_EINVAL),       # B*H*N*d >= 2^31
+    (dict(B=1024, H=1024, N=1024, d=64), attn.ATTN_EINVAL),    # B*H*ceil(N/128) >= 2^23 (grid limit)
+    (dict(B=1, H=1, N=1 << 22, d=128), attn.ATTN_EINVAL),      # one head's fp32 rows >= 2 GiB
 ])
 def test_fwd_rejects_before_launch(kw, expect):
     assert fwd(**kw) == expect
@@ -60,7 +61,7 @@ def test_fwd_rejects_before_launch(kw, expect):
 
 def test_bwd_rejects_before_launch():
     L = attn.lib()
-    ws = L.attn_bwd_workspace_bytes(1, 1, 16, 64)
+    ws = L.attn_bwd_workspace_bytes(1, 1, 16, 64, attn.ATTN_F32)
     assert ws == 256
     args = lambda d=64, wsb=ws, g=attn.ATTN_F32, w=P, dt=attn.ATTN_BF16: (
         P, P, P, P, P, P, dt, 1, 1, 16, d, 0.125, 1, P, P, P, g, w, ctypes.c_size_t(wsb), None)
@@ -95,7 +96,7 @@ def test_blocksparse_rejects_bad_masks_before_launch():
     assert fwd(heads=5) == attn.ATTN_EINVAL                  # neither 1 nor B*H = 6
     assert fwd(heads=6, d=96) == attn.ATTN_EUNSUPPORTED
     assert fwd(heads=6, causal=2) == attn.ATTN_EINVAL
-    ws = L.attn_bwd_workspace_bytes(2, 3, 300, 64)
+    ws = L.attn_bwd_workspace_bytes(2, 3, 300, 64, attn.ATTN_F32)
     bwd = lambda mask=M, heads=1, wsb=ws: L.attn_bwd_blocksparse(
         P, P, P, P, P, P, attn.ATTN_BF16, 2, 3, 300, 64, 0.125, 0, mask, heads, P, P, P, attn.ATTN_F32, P,
         ctypes.c_size_t(wsb), None)
@@ -121,9 +122,80 @@ def test_fp8_rejects_before_launch():
 def test_workspace_sizes():
     L = attn.lib()
     rows = 4 * 16 * 4096
-    assert L.attn_bwd_workspace_bytes(4, 16, 4096, 128) == rows * 4
-    assert L.attn_bwd_workspace_bytes(1, 1, 3, 64) == 256
-    assert L.attn_bwd_workspace_bytes(0, 16, 4096, 128) == 0
+    for g in (attn.ATTN_F32, attn.ATTN_BF16):       # D only, whatever the gradients' dtype
+        assert L.attn_bwd_workspace_bytes(4, 16, 4096, 128, g) == rows * 4
+        assert L.attn_bwd_workspace_bytes(1, 1, 3, 64, g) == 256
+        assert L.attn_bwd_workspace_bytes(0, 16, 4096, 128, g) == 0
+    assert L.attn_bwd_workspace_bytes(1, 1, 3, 64, 7) == 0       # not a dtype
+    # more than 2^31 elements in all: valid (heads are addressed with 64-bit offsets)
+    assert L.attn_bwd_workspace_bytes(1, 4097, 4096, 128, attn.ATTN_F32) == 4097 * 4096 * 4
+    assert fwd(B=1, H=4097, N=4096, d=128, q=MIS) == attn.ATTN_EINVAL      # reaches the pointer checks
+
+
+# ---- the Python binding checks every tensor's shape and dtype before it touches a device ----
+def _t(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["k_shape", "v_dtype", "out_shape", "lse_dtype", "lse_shape"])
+def test_binding_rejects_mismatched_forward_buffers(case):
+    import torch
+    q = _t((1, 2, 40, 64))
+    kw = dict(k=_t((1, 2, 40, 64)), v=_t((1, 2, 40, 64)))
+    extra = {}
+    if case == "k_shape":
+        kw["k"] = _t((1, 2, 41, 64))
+    elif case == "v_dtype":
+        kw["v"] = _t((1, 2, 40, 64), torch.float32)
+    elif case == "out_shape":
+        extra["out"] = _t((1, 2, 40, 80))
+    elif case == "lse_dtype":
+        extra["lse"] = _t((1, 2, 40), torch.bfloat16)
+    else:
+        extra["lse"] = _t((1, 2, 41), torch.float32)
+    with pytest.raises(ValueError, match="must"):
+        attn.attn_fwd(q, kw["k"], kw["v"], **extra)
+
+
+@pytest.mark.parametrize("case", ["dq_dtype", "dk_shape", "do_dtype", "lse_shape", "workspace_small", "grad_dtype"])
+def test_binding_rejects_mismatched_backward_buffers(case):
+    import torch
+    shp = (1, 2, 40, 64)
+    q, k, v, o, do = (_t(shp) for _ in range(5))
+    lse = _t(shp[:-1], torch.float32)
+    kw = {}
+    if case == "dq_dtype":
+        kw["dq"] = _t(shp, torch.bfloat16)           # default gradients are fp32
+    elif case == "dk_shape":
+        kw["dk"] = _t((1, 2, 40, 32), torch.float32)
+    elif case == "do_dtype":
+        do = _t(shp, torch.float32)
+    elif case == "lse_shape":
+        lse = _t((1, 2, 39), torch.float32)
+    elif case == "workspace_small":
+        kw["workspace"] = _t((16,), torch.uint8)
+    else:
+        kw["grad_dtype"] = torch.float16
+    with pytest.raises((ValueError, TypeError), match="must"):
+        attn.attn_bwd(q, k, v, o, do, lse, **kw)
+
+
+def test_binding_rejects_mismatched_split_backward_buffers():
+    import torch
+    shp = (1, 2, 40, 64)
+    q, k, v, o, do = (_t(shp) for _ in range(5))
+    lse, D = _t(shp[:-1], torch.float32), _t(shp[:-1], torch.float32)
+    with pytest.raises(ValueError, match="must"):
+        attn.attn_bwd_dkdv(q, k, v, do, lse, _t(shp[:-1], torch.bfloat16))
+    with pytest.raises(ValueError, match="must"):
+        attn.attn_bwd_dq(q, k, v, do, lse, D, dq=_t(shp, torch.bfloat16))
+    with pytest.raises(ValueError, match="must"):
+        attn.attn_bwd_dq_d(q, k, v, _t((1, 2, 40, 128)), do, lse)
+    with pytest.raises(ValueError, match="must"):
+        attn.attn_bwd_main(q, k, v, do, lse, D, dv=_t((1, 1, 40, 64), torch.float32))
+    with pytest.raises(ValueError, match="must"):
+        attn.attn_bwd_preprocess(o, _t((1, 2, 40, 80)))
 
 
 def test_status_strings():
