@@ -15,13 +15,14 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP, ATTN_ENOSPACE = 0, 1, 2, 3, 4
 ATTN_F32, ATTN_BF16 = 0, 1
 
 EXPORTED = ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_d", "attn_bwd_main",
             "attn_bwd_workspace_bytes", "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
-            "attn_fwd_fp8", "attn_status_str", "attn_last_hip_error")
+            "attn_fwd_fp8", "attn_bwd_noalloc", "attn_status_str", "attn_last_hip_error")
 MASK_BLOCK = 128        # ATTN_MASK_BLOCK: rows and keys per block-mask entry
+NOALLOC_MAX_ROWS = 4 * 1024 * 1024      # ATTN_NOALLOC_MAX_ROWS: B*H*N limit of attn_bwd_noalloc
 
 _lib = None
 
@@ -65,8 +66,10 @@ def lib():
         L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, vp, i, vp,
                                            sz, vp]
         L.attn_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, i, i, i, i, f, i, vp, vp, vp]
+        L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, i, vp]
         for name in ("attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_d", "attn_bwd_main",
-                     "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse", "attn_fwd_fp8"):
+                     "attn_bwd", "attn_fwd_blocksparse", "attn_bwd_blocksparse", "attn_fwd_fp8",
+                     "attn_bwd_noalloc"):
             getattr(L, name).restype = i
         L.attn_status_str.argtypes = [i]
         L.attn_status_str.restype = ctypes.c_char_p
@@ -266,6 +269,25 @@ def attn_bwd(q, k, v, o, do, lse, scale=None, causal=False, grad_dtype=torch.flo
     _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
           float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), gdt, _ptr(workspace),
           ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(q, stream))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale=None, causal=False, stream=None):
+    """attn_bwd without a workspace: the library's static device scratch holds D, so the C call
+    allocates nothing (the caller passes the gradient buffers, of one dtype: float32 or bfloat16).
+    B*H*N must not exceed NOALLOC_MAX_ROWS.  Calls that overlap on one GPU race on the scratch."""
+    B, H, N, d = _shape(q)
+    _dt(q)
+    _expect_like_q(q, k=k, v=v, o=o, do=do)
+    _expect_rows(q, lse=lse)
+    gdt = _gdt(dq.dtype)
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, n, q.shape, dq.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_inputs(q, k, v, o, do, lse, dq, dk, dv)
+    _call("attn_bwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dt(q), B, H, N, d,
+          float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), gdt, _stream(q, stream))
     return dq, dk, dv
 
 

@@ -4,12 +4,43 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/attn.h"
 #include "attn_launch.h"
+
+// Device scratch of attn_bwd_noalloc: the backward's one workspace buffer (the fp32 D
+// rows, B*H*N floats) as a static array, so that entry point never allocates.  Each GPU
+// holds its own copy until the process ends; host code reaches it only through the
+// address hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).
+static constexpr size_t kNoAllocRows = (size_t)ATTN_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) float scratch[kNoAllocRows];
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Per-device address of `scratch`, looked up once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_for_current_device(float** out)
+{
+    int dev = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* ptr = nullptr;
+        if (hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)); e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        p = static_cast<float*>(ptr);
+        g_scratch_ptr[dev].store(p, std::memory_order_release);   // same value whichever thread wins
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -49,6 +80,7 @@ const char* attn_status_str(attn_status s)
         case ATTN_EINVAL: return "invalid argument";
         case ATTN_EUNSUPPORTED: return "unsupported configuration";
         case ATTN_EHIP: return "HIP runtime error";
+        case ATTN_ENOSPACE: return "request exceeds the static scratch of the allocation-free entry point";
     }
     return "unknown status";
 }
@@ -187,6 +219,19 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
 {
     return bwd_all(Q, K, V, O, dO, LSE, dt, B, H, N, d, scale, causal, nullptr, 0, dQ, dK, dV, grad_dt, workspace,
                    workspace_bytes, stream);
+}
+
+attn_status attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, attn_dtype dt, int B, int H, int N, int d, float scale, int causal,
+                             void* dQ, void* dK, void* dV, attn_dtype grad_dt, void* stream)
+{
+    attn_status s = check_shape(B, H, N, d);
+    if (s != ATTN_OK) return s;
+    if ((size_t)B * (size_t)H * (size_t)N > kNoAllocRows) return ATTN_ENOSPACE;
+    float* ws = nullptr;
+    if (attn_status r = from_hip(scratch_for_current_device(&ws)); r != ATTN_OK) return r;
+    return bwd_all(Q, K, V, O, dO, LSE, dt, B, H, N, d, scale, causal, nullptr, 0, dQ, dK, dV, grad_dt, ws,
+                   kNoAllocRows * sizeof(float), stream);
 }
 
 attn_status attn_fwd_fp8(const void* Q, const void* K, const void* V, float q_descale, float k_descale,

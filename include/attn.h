@@ -47,7 +47,8 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_EINVAL = 1,        /* bad pointer, size, alignment, scale or flag   */
     ATTN_EUNSUPPORTED = 2,  /* valid request the library does not implement */
-    ATTN_EHIP = 3           /* a HIP runtime call failed                     */
+    ATTN_EHIP = 3,          /* a HIP runtime call failed                     */
+    ATTN_ENOSPACE = 4       /* more than attn_bwd_noalloc's static scratch   */
 } attn_status;
 
 typedef enum {
@@ -134,6 +135,27 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                      int B, int H, int N, int d, float scale, int causal,
                      void* dQ, void* dK, void* dV, attn_dtype grad_dt,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same operation, arguments, kernels and results as attn_bwd, but
+ * without the workspace argument: the one scratch buffer the backward needs (the
+ * fp32 D rows, B*H*N floats) is a static device array of ATTN_NOALLOC_MAX_ROWS
+ * floats (16 MiB) inside the library, one copy per GPU, held until the process
+ * ends.  Its address is looked up once per device, on the first call made with
+ * that device current.  B*H*N > ATTN_NOALLOC_MAX_ROWS gives ATTN_ENOSPACE and
+ * nothing is launched; other errors as attn_bwd.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  Nothing in the scratch
+ * needs to start at zero: each call overwrites the D rows it reads.  Every call
+ * on one GPU shares that GPU's scratch, so calls that overlap on one GPU (on
+ * streams not ordered with each other, or from several host threads) race and
+ * must be serialised by the caller. */
+#define ATTN_NOALLOC_MAX_ROWS (4 * 1024 * 1024)
+
+attn_status attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                             const void* dO, const float* LSE, attn_dtype dt,
+                             int B, int H, int N, int d, float scale, int causal,
+                             void* dQ, void* dK, void* dV, attn_dtype grad_dt, void* stream);
 
 /* Block-sparse attention.  FlashAttention-2 review, 'sparse/hybrid' answer,
  * section 3 (1) (Sparse FlashAttention): the score matrix is cut into blocks,

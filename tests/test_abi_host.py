@@ -119,6 +119,16 @@ def test_fp8_rejects_before_launch():
     assert f(q=NUL) == attn.ATTN_EINVAL
 
 
+def test_noalloc_rejects_before_launch():
+    L = attn.lib()
+    f = lambda B=1, H=2, N=64, d=128, q=P, dt=attn.ATTN_BF16: L.attn_bwd_noalloc(
+        q, P, P, P, P, P, dt, B, H, N, d, 0.1, 1, P, P, P, attn.ATTN_F32, None)
+    # more rows than the static scratch holds: rejected before any HIP call
+    assert f(B=1, H=4, N=attn.NOALLOC_MAX_ROWS // 4 + 1, d=64) == attn.ATTN_ENOSPACE
+    assert f(d=96) == attn.ATTN_EUNSUPPORTED
+    assert f(N=0) == attn.ATTN_EINVAL
+
+
 def test_workspace_sizes():
     L = attn.lib()
     rows = 4 * 16 * 4096
@@ -200,7 +210,7 @@ def test_binding_rejects_mismatched_split_backward_buffers():
 
 def test_status_strings():
     L = attn.lib()
-    for s in range(4):
+    for s in range(5):
         assert L.attn_status_str(s)
     assert L.attn_status_str(99) == b"unknown status"
     assert L.attn_last_hip_error() == 0
