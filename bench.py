@@ -58,7 +58,8 @@ class Workload:
     def __init__(self, cfg, dev):
         self.cfg = cfg
         q, k, v, do = config_inputs(cfg)
-        self.q, self.k, self.v, self.do = (t.to(dev) for t in (q, k, v, do))
+        self.q, self.k, self.v = (t.to(dev) for t in (q, k, v))
+        self.do = do.to(dev) if do is not None else None          # forward-only workloads have no dO
         B, H, N, d = q.shape
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
@@ -206,6 +207,54 @@ def cpu_baseline(cfg, budget_s=12.0):
                       f"N={cfg.N}, d={cfg.d}, causal={cfg.causal}; {dt:.1f} s wall"}
 
 
+def workload_entry(idx, dev, steps, warmup):
+    """One workload's line: per-kernel mean HIP-event time, TFLOP/s and fraction of the bf16 peak
+    (algorithmic FLOPs: 4 N^2 d per head forward, the backward's 2.5x split as in main())."""
+    cfg = CONFIGS[idx]
+    w = Workload(cfg, dev)
+    wall, per = w.measure(steps, warmup)
+    kflops = {"attn_fwd": w.fl_fwd, "attn_bwd_dkdv": 2.0 * w.fl_fwd, "attn_bwd_dq_d": 0.5 * w.fl_fwd}
+    ent = {"workload": f"{cfg.name} (seed {cfg.seed})", "steps": steps, "ms_per_step": round(wall * 1e3, 4),
+           "kernels": {n: {"us": round(t * 1e6, 2), "tflops": round(kflops[n] / t / 1e12, 2),
+                           "frac_peak": round(kflops[n] / t / 1e12 / PEAK_BF16_TFLOPS, 4)} for n, t in per.items()},
+           "fwd_tflops": round(w.fl_fwd / per["attn_fwd"] / 1e12, 2),
+           "fwd_frac_peak": round(w.fl_fwd / per["attn_fwd"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if cfg.backward:
+        tb = sum(t for n, t in per.items() if n != "attn_fwd")
+        ent.update(bwd_us=round(tb * 1e6, 2), bwd_tflops=round(w.fl_bwd / tb / 1e12, 2),
+                   bwd_frac_peak=round(w.fl_bwd / tb / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   value=round((w.fl_fwd + w.fl_bwd) / wall / 1e12, 2))
+    else:
+        ent.update(value=round(w.fl_fwd / wall / 1e12, 2))
+    log(f"bench: workload {idx} step {wall * 1e3:.3f} ms; " +
+        ", ".join(f"{n} {t * 1e6:.1f} us ({kflops[n] / t / 1e12:.0f} TFLOP/s)" for n, t in per.items()))
+    del w
+    torch.cuda.empty_cache()
+    return ent
+
+
+def trace_summary(path, skip):
+    """Per-kernel launch statistics from a rocprofv3 kernel trace (CSV), over the launches after the
+    first `skip` of each kernel (the warm-up: a fresh process's first launches run at lower clocks).
+    Prints a markdown table; needs no GPU."""
+    import csv
+    import statistics
+    durs = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            durs.setdefault(name, []).append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+    print(f"| kernel | launches (all) | launches kept | average (us) | median (us) | min (us) | max (us) |")
+    print("|---|---|---|---|---|---|---|")
+    for name, ts in sorted(durs.items(), key=lambda kv: -sum(e - b for b, e in kv[1])):
+        ts.sort()
+        kept = [(e - b) / 1e3 for b, e in ts[skip:]]
+        if not kept:
+            continue
+        print(f"| `{name}` | {len(ts)} | {len(kept)} | {statistics.mean(kept):.1f} | {statistics.median(kept):.1f} | "
+              f"{min(kept):.1f} | {max(kept):.1f} |")
+
+
 def load_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it matches these sources."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
@@ -236,7 +285,16 @@ def main():
                     help="only the block-sparse measurement (prints its JSON object; for profiling)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a plain 1 GiB device copy (rocprofv3 counter calibration)")
+    ap.add_argument("--no-other", action="store_true", help="skip workloads 2 and 5")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-kernel statistics of a rocprofv3 kernel trace (no GPU needed) and exit")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="with --trace-summary: leave out the first SKIP launches of each kernel")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.skip)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU only (asked for {args.gpus}); "
@@ -322,7 +380,7 @@ def main():
 
     if cfg.index == 3 and not args.no_secondary:
         cfg4 = CONFIGS[4]
-        del w
+        w = None
         torch.cuda.empty_cache()
         log("bench: secondary workload 4 (N=16384)")
         w4 = Workload(cfg4, dev)
@@ -340,6 +398,12 @@ def main():
             "kernels_us": {n: round(t * 1e6, 2) for n, t in per4.items()},
         }
         log(f"bench: N=16384 step {wall4 * 1e3:.3f} ms; " + ", ".join(f"{n} {t * 1e6:.1f} us" for n, t in per4.items()))
+
+    if cfg.index == 3 and not args.no_other:
+        # the other two bf16 workloads: 2 (d = 64, non-causal, forward) and 5 (d = 80, causal, fwd + bwd)
+        w = None
+        torch.cuda.empty_cache()
+        out["other_workloads"] = {f"workload_{i}": workload_entry(i, dev, args.steps, args.warmup) for i in (2, 5)}
 
     if cfg.index == 3 and not args.no_sparse:
         torch.cuda.empty_cache()

@@ -8,8 +8,8 @@
 // exchanges partial results with other waves): FlashAttention-2 review, the
 // Split-K vs Split-Q answer, section 2.
 //
-// gfx950 mapping shared by both kernels (one workgroup = 4 waves = 256 threads
-// per block of 128 query rows; each wave owns 32 rows):
+// gfx950 mapping shared by the kernels (each wave owns 32 query rows; a workgroup
+// holds 4 waves, or 8 for the dense bf16 walks):
 //   * The wave computes S^T = K Q^T with MFMA 32x32 tiles, so every lane of the
 //     accumulator holds ONE query and 16 keys.  The running max, running sum and
 //     rescale factor are then per-lane scalars; the only cross-lane step per
@@ -24,8 +24,9 @@
 //     the element mask runs only on tiles that cross the diagonal or N.
 //
 // fwd_kernel_f32 (fp32 inputs, MFMA 32x32x2 f32) stages K and V through
-// registers into padded LDS (V transposed, key fastest); fwd_kernel_bf16 below
-// is the bf16 hot path.
+// registers into padded LDS (V transposed, key fastest).  bf16 (the hot path):
+// fwd_kernel_bf16_pipe for dense walks, fwd_kernel_bf16_sparse for block-sparse
+// ones, with the same arithmetic.
 #include <float.h>
 
 #include "../../include/attn.h"
@@ -354,15 +355,14 @@ __global__ __launch_bounds__(256) void fwd_kernel_f32(const float* __restrict__ 
 }
 
 // ----------------------------------------------------------------------------
-// bf16 forward (the hot path).  Same per-lane softmax as above; K and V tiles go
+// bf16 forward, block-sparse walks.  Same per-lane softmax as above; K and V tiles go
 // straight from HBM/L2 into swizzled LDS rows (direct-to-LDS loads, no staging
 // registers, no transposing stores) and V^T reaches the MFMA through transpose
-// reads.  sK0/sK1/sV0/sV1 are separate __shared__ objects and the loop is
-// unrolled by two, so the compiler can tell the next tile's in-flight loads from
-// the current tile's reads.  Dense walks: 8 waves (256 query rows) per workgroup,
-// one workgroup per CU, so each K/V tile load serves 256 rows (measured about 2%
-// faster than two 4-wave workgroups per CU).  Block-sparse walks: 4 waves (128
-// rows, one mask block), two workgroups per CU.  <= 256 registers per wave.
+// reads.  sK0/sK1/sV0/sV1 are separate __shared__ objects and the loop is unrolled by
+// two, so the compiler can tell the next tile's in-flight loads from the current
+// tile's reads.  4 waves (128 rows, one mask block) per workgroup, two workgroups per
+// CU, <= 256 registers per wave.  Dense walks take fwd_kernel_bf16_pipe below, which
+// does the same arithmetic in the same order (an all-kept mask gives identical bits).
 // ----------------------------------------------------------------------------
 template <int D, int WAVES>
 struct FwdBf16Cfg {
@@ -374,19 +374,18 @@ struct FwdBf16Cfg {
     static_assert(4 * T_BYTES <= 80 * 1024, "two workgroups per CU");
 };
 
-template <bool SPARSE> constexpr int fwd_bf16_waves() { return SPARSE ? 4 : 8; }
-
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(64 * fwd_bf16_waves<SPARSE>(), 8 / fwd_bf16_waves<SPARSE>())
-void fwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2)
+void fwd_kernel_bf16_sparse(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                                                           const bf16* __restrict__ V, bf16* __restrict__ O,
                                                           float* __restrict__ LSE, int N, int nqblk, float c,
                                                           int negate_q, const uint8_t* __restrict__ bmask,
                                                           long mhead, int slots)
 {
-    constexpr int WAVES = fwd_bf16_waves<SPARSE>();
+    constexpr bool SPARSE = true;
+    constexpr int WAVES = 4;
     using C = FwdBf16Cfg<D, WAVES>;
-    static_assert(!SPARSE || (kMaskBlock == 2 * C::BN && kMaskBlock == C::BM), "mask block = query block");
+    static_assert(kMaskBlock == 2 * C::BN && kMaskBlock == C::BM, "mask block = query block");
     constexpr int RB = C::RB;
     constexpr uint32_t ROWB = D * 2;
     constexpr float NEG_INF = -__builtin_inff();
@@ -542,22 +541,7 @@ void fwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
     };
 
-    if constexpr (!SPARSE) {
-        auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
-            wait_vmem_all();                            // this wave's loads of tile j landed
-            __syncthreads();                            // everyone's; tile j-1 fully read
-            if (j + 1 < ntiles) issue_tile(j + 1, kn, vn);
-            if (!(CAUSAL && j * C::BN > q0w + 31))      // else every key follows this wave's rows
-                tile_body(j, kc, vc);
-        };
-        issue_tile(0, sK0, sV0);
-        int j = 0;
-        for (; j + 1 < ntiles; j += 2) {
-            step(j, sK0, sV0, sK1, sV1);
-            step(j + 1, sK1, sV1, sK0, sV0);
-        }
-        if (j < ntiles) step(j, sK0, sV0, sK1, sV1);
-    } else {
+    {
         // jn: the next tile to visit (ntiles if none)
         auto step = [&](int j, int jn, const char* kc, const char* vc, char* kn, char* vn) {
             wait_vmem_all();
@@ -604,6 +588,260 @@ void fwd_kernel_bf16(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 forward, dense walks: the same arithmetic as fwd_kernel_bf16 (same products in
+// the same order, same roundings, same rescale decisions: bit-identical results),
+// software-pipelined across key tiles so that each wave's softmax runs under its own
+// MFMAs instead of between them.  Iteration j of a wave:
+//   [A]  S_{j+1} = K_{j+1} Q^T   (16 MFMAs at d = 128)  with  exp2 of S_j, keys 0-31
+//   [B1] O^T += V_j^T P_j^T, keys 0-31                   with  exp2 of S_j, keys 32-63
+//   [B2] O^T += V_j^T P_j^T, keys 32-63                  with  the row max of S_{j+1}
+// and the rare rescale of O and l (lazy, threshold 2^8) at the top, before the
+// exponentials of S_j need the reference max.  K runs one tile ahead of V: at the top
+// of iteration j (one barrier) K_{j+2} and V_{j+1} are issued into the buffers that
+// iteration j-1 finished reading, and iteration j reads K_{j+1} and V_j.
+// 8 waves (256 query rows) per workgroup, 32 rows per wave, two waves per SIMD.
+// ----------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1)
+void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                          bf16* __restrict__ O, float* __restrict__ LSE, int N, int nqblk, float c, int negate_q,
+                          int slots)
+{
+    constexpr int WAVES = 8;
+    using C = FwdBf16Cfg<D, WAVES>;
+    static_assert(C::NKT == 2, "two 32-key halves per tile");
+    constexpr int RB = C::RB, NKS = C::NKS, NDT = C::NDT;
+    constexpr uint32_t ROWB = D * 2;
+    constexpr float NEG_INF = -__builtin_inff();
+    __shared__ __attribute__((aligned(1024))) char sK0[C::T_BYTES], sK1[C::T_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sV0[C::T_BYTES], sV1[C::T_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+
+    int head, qb;
+    block_coords<CAUSAL, true>(blockIdx.x, gridDim.x, nqblk, slots, head, qb);
+    const int q0 = qb * C::BM;
+    const int q0w = q0 + 32 * wave;
+    const int myq = q0w + l32;
+    const size_t hoff = (size_t)head * (size_t)N * D;
+    const bf16* __restrict__ Kh = K + hoff;
+    const bf16* __restrict__ Vh = V + hoff;
+    TileLane<RB, NKS, NDT, true> tl;
+    tl.init(lane);
+
+    // Q fragments (B operand of S^T = K Q^T), sign-flipped for a negative scale
+    bf16x8 qf[NKS];
+    {
+        const auto rq = make_rsrc(Q + hoff, (uint32_t)N * ROWB);
+        const uint32_t ro = (uint32_t)myq * ROWB + 16 * h;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            u32x4 raw = buf_ld16(rq, ro + 32 * s);
+            if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+            qf[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    f32x16 oacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+    float mc = NEG_INF, l = 0.f;
+
+    const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+    const int ntiles = (kv_end + C::BN - 1) / C::BN;
+    // this wave's last tile (causal: the last one holding a key at or before its last row)
+    const int jlast = CAUSAL ? min(ntiles - 1, (q0w + 31) / C::BN) : ntiles - 1;
+
+    auto issue = [&](const bf16* __restrict__ base, int j, char* tile) {
+        const int kv0 = j * C::BN;
+        const uint32_t bytes = (uint32_t)(N - kv0) * ROWB;        // rows past N read as zeros
+        dma_rows<D, RB, true>(make_rsrc(base + (size_t)kv0 * D, bytes), tile, wave * (C::BN / WAVES),
+                              C::BN / WAVES, lane);
+    };
+    auto need_mask = [&](int j) { return (CAUSAL && j * C::BN + C::BN - 1 > q0w) || (j * C::BN + C::BN > N); };
+    // lane: query myq, keys kv0 + 4 h + cr with cr = 32 kt + 8 (r/4) + r%4; masked when cr > bound
+    auto apply_mask = [&](f32x16 (&sacc)[2], int j) {
+        const int kv0 = j * C::BN;
+        const int bound = CAUSAL ? min(myq, N - 1) - kv0 - 4 * h : N - 1 - kv0 - 4 * h;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (32 * kt + 8 * (r >> 2) + (r & 3) > bound) sacc[kt][r] = NEG_INF;
+    };
+    // the row max of a score tile, scaled to log2 units (both lanes of a query agree)
+    auto row_max = [&](const float (&mx4)[4]) {
+        float mx = max3f(mx4[0], mx4[1], fmaxf(mx4[2], mx4[3]));
+        mx = fmaxf(mx, xor32(mx));
+        return (mx == NEG_INF) ? NEG_INF : mx * c;
+    };
+    // the score product of tile j+1 as NKS * 2 MFMAs, with `work(i)` issued after MFMA i;
+    // K fragments are read PF MFMAs ahead through a ring
+    auto scores = [&](f32x16 (&sacc)[2], const char* sK, auto&& work) __attribute__((always_inline)) {
+        constexpr int NM = NKS * 2, PF = 4;
+        bf16x8 ring[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) ring[i] = tl.row(sK, 32 * (i % 2), i / 2);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            const int s = i / 2, kt = i % 2;
+            const bf16x8 a = ring[i % PF];
+            if (i + PF < NM) ring[i % PF] = tl.row(sK, 32 * ((i + PF) % 2), (i + PF) / 2);
+            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s == 0 ? f32x16{} : sacc[kt], 0, 0, 0);
+            work(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // 16 max3 of a score tile into four partial maxima, `x` = slices of eight
+    auto max_slice = [&](float (&mx4)[4], const f32x16 (&sacc)[2], int x) __attribute__((always_inline)) {
+        const int kt = x >> 3, r = 2 * (x & 7);
+        mx4[r >> 2] = max3f(mx4[r >> 2], sacc[kt][r], sacc[kt][r + 1]);
+    };
+
+    // prologue: K_0, V_0, K_1 in flight; S_0 and its (unmasked) row max
+    f32x16 sA[2], sB[2];
+    float mxc_next;
+    issue(Kh, 0, sK0);
+    issue(Vh, 0, sV0);
+    if (ntiles > 1) issue(Kh, 1, sK1);
+    wait_vmem_all();
+    __syncthreads();
+    scores(sA, sK0, [&](int) {});
+    {
+        float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+        for (int x = 0; x < 16; ++x) max_slice(mx4, sA, x);
+        mxc_next = row_max(mx4);
+    }
+
+    // One iteration: scur = S_j, snext <- S_{j+1}; sKn holds K_{j+1}, sVc V_j.  On a wave's last
+    // tile, [A] still runs on whatever the K buffer holds (in bounds) and its result is never
+    // used: a branch around it would make the compiler copy the live score tile at the join.
+    auto body = [&](int j, f32x16 (&scur)[2], f32x16 (&snext)[2], const char* sKn, const char* sVc)
+        __attribute__((always_inline)) {
+        // tiles crossing the diagonal or N (rare): mask S_j in place and take its max again
+        float mxc = mxc_next;
+        if (need_mask(j)) {
+            apply_mask(scur, j);
+            float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+            for (int x = 0; x < 16; ++x) max_slice(mx4, scur, x);
+            mxc = row_max(mx4);
+        }
+        // the reference max moves only when the tile's max exceeds it by 2^kLazyLog2
+        if (__builtin_amdgcn_ballot_w64(mxc > mc + kLazyLog2) != 0) {
+            const float mnew = fmaxf(mc, mxc);
+            const float alpha = fast_exp2(mc - mnew);               // 0 on the first tile
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            mc = mnew;
+        }
+        const float ms = mc;
+        bf16x8 pf[2][2];
+        float ls[2] = {0.f, 0.f};
+        // exp2 of element r of key half kt (a masked -inf gives 0: mc is finite, c >= FLT_MIN);
+        // P in bf16 and the row sum over exactly those values, eight elements at a time
+        auto expo = [&](int kt, int r) __attribute__((always_inline)) {
+            scur[kt][r] = fast_exp2(fmaf(scur[kt][r], c, -ms));
+        };
+        auto pack = [&](int kt, int s2) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[kt][s2][e] = to_bf16(scur[kt][8 * s2 + e]);
+            const u32x4 w = __builtin_bit_cast(u32x4, pf[kt][s2]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ls[s2] = sum2_bf16(w[x], ls[s2]);
+        };
+        // [A] the next tile's score MFMAs with the exponentials of keys 0-31
+        scores(snext, sKn, [&](int i) __attribute__((always_inline)) {
+            constexpr int NM = NKS * 2;
+#pragma unroll
+            for (int r = 16 * i / NM; r < 16 * (i + 1) / NM; ++r) {
+                expo(0, r);
+                if (r == 7) pack(0, 0);
+                if (r == 15) pack(0, 1);
+            }
+        });
+        // O^T += V^T P^T: product t = (2 kt + s2) NDT + dt; V^T fragments PF products ahead
+        constexpr int NT = 4 * NDT, PF = 4;
+        auto tfrag = [&](int t) __attribute__((always_inline)) {
+            return tl.tr(sVc, 32 * (t / (2 * NDT)) + 16 * ((t / NDT) & 1), t % NDT);
+        };
+        bf16x8 ring[PF];
+#pragma unroll
+        for (int t = 0; t < PF; ++t) ring[t] = tfrag(t);
+        float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const bf16x8 a = ring[t % PF];
+            if (t + PF < NT) ring[t % PF] = tfrag(t + PF);
+            const int kt = t / (2 * NDT), s2 = (t / NDT) & 1, dt = t % NDT;
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][s2], oacc[dt], 0, 0, 0);
+            if (t < 2 * NDT) {
+                // [B1] keys 0-31 of P V, with the exponentials of keys 32-63
+#pragma unroll
+                for (int r = 16 * t / (2 * NDT); r < 16 * (t + 1) / (2 * NDT); ++r) {
+                    expo(1, r);
+                    if (r == 7) pack(1, 0);
+                    if (r == 15) pack(1, 1);
+                }
+            } else {
+                // [B2] keys 32-63 of P V, with the next tile's (unmasked) row max
+                const int u = t - 2 * NDT;
+#pragma unroll
+                for (int x = 16 * u / (2 * NDT); x < 16 * (u + 1) / (2 * NDT); ++x) max_slice(mx4, snext, x);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mxc_next = row_max(mx4);
+        l += ls[0] + ls[1];
+    };
+
+    auto step = [&](int j, f32x16 (&scur)[2], f32x16 (&snext)[2], const char* sKn, const char* sVc, char* sKl,
+                    char* sVl) __attribute__((always_inline)) {
+        wait_vmem_all();                            // this wave's loads of K_{j+1} and V_j landed
+        __syncthreads();                            // everyone's; iteration j-1 fully read
+        if (j + 2 < ntiles) issue(Kh, j + 2, sKl);
+        if (j + 1 < ntiles) issue(Vh, j + 1, sVl);
+        if (j <= jlast) body(j, scur, snext, sKn, sVc);
+    };
+    // even j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1 (odd j mirrored)
+    int j = 0;
+    for (; j + 1 < ntiles; j += 2) {
+        step(j, sA, sB, sK1, sV0, sK0, sV1);
+        step(j + 1, sB, sA, sK0, sV1, sK1, sV0);
+    }
+    if (j < ntiles) step(j, sA, sB, sK1, sV0, sK0, sV1);
+
+    // epilogue: one division by l, O and LSE written once
+    const float lt = l + xor32(l);
+    const float inv = 1.0f / lt;
+    if (myq < N) {
+        bf16* dst = O + hoff + (size_t)myq * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * dt + 8 * g + 4 * h;
+                if (d0 < D) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = to_bf16(oacc[dt][4 * g + e] * inv);
+                    *reinterpret_cast<bf16x4*>(dst + d0) = v;
+                }
+            }
+        if (h == 0) LSE[(size_t)head * N + myq] = (mc + __log2f(lt)) * kLn2;
+    }
+}
+
 template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd_f32(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
                                  float scale, const uint8_t* bmask, long mhead, hipStream_t st)
@@ -623,13 +861,18 @@ template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int N,
                                   float scale, const uint8_t* bmask, long mhead, hipStream_t st)
 {
-    using C = FwdBf16Cfg<D, fwd_bf16_waves<SPARSE>()>;
-    const int nqblk = (N + C::BM - 1) / C::BM;
-    hipLaunchKernelGGL((fwd_kernel_bf16<D, CAUSAL, SPARSE>), dim3(nqblk * BH), dim3(64 * fwd_bf16_waves<SPARSE>()), 0,
-                       st, (const bf16*)Q,
-                       (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk,
-                       fmaxf(fabsf(scale) * kLog2e, FLT_MIN),       // scale 0: -inf * c stays -inf
-                       (int)(scale < 0.f), bmask, mhead, tune_lookup(kTuneFwdBf16, D, CAUSAL, N).slots);
+    const float c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);        // scale 0: -inf * c stays -inf
+    const int negq = scale < 0.f;
+    const int slots = tune_lookup(kTuneFwdBf16, D, CAUSAL, N).slots;
+    if constexpr (SPARSE) {
+        const int nqblk = (N + FwdBf16Cfg<D, 4>::BM - 1) / FwdBf16Cfg<D, 4>::BM;
+        hipLaunchKernelGGL((fwd_kernel_bf16_sparse<D, CAUSAL>), dim3(nqblk * BH), dim3(256), 0, st, (const bf16*)Q,
+                           (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk, c, negq, bmask, mhead, slots);
+    } else {
+        const int nqblk = (N + FwdBf16Cfg<D, 8>::BM - 1) / FwdBf16Cfg<D, 8>::BM;
+        hipLaunchKernelGGL((fwd_kernel_bf16_pipe<D, CAUSAL>), dim3(nqblk * BH), dim3(512), 0, st, (const bf16*)Q,
+                           (const bf16*)K, (const bf16*)V, (bf16*)O, LSE, N, nqblk, c, negq, slots);
+    }
     return hipGetLastError();
 }
 
