@@ -456,8 +456,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     const bf16* __restrict__ Qh = Q + hoff;
     const bf16* __restrict__ dOh = dO + hoff;
     const float c2 = scale * kLog2e;
-    TileLane<RB, C::NKS, C::NDT, false> tl;
-    tl.init(lane);
+    // fragment offsets of this wave's own row bands: keys 32 kg.. of K/V, queries 32 qh.. of Q/dO
+    TileLane<RB, C::NKS, C::NDT, false> tlk, tlq;
+    tlk.init(lane, 32 * kg);
+    tlq.init(lane, 32 * qh);
 
     // the workgroup's K and V rows to LDS (16 rows per wave each); after the first item
     // the previous item's epilogue has already issued them
@@ -502,7 +504,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         {
             constexpr int NF = 2 * NKS;                 // f: s = f / 2; A (Q rows), then B (K rows)
             auto frag = [&](int f) __attribute__((always_inline)) {
-                return tl.row((f & 1) ? sK : sQ, (f & 1) ? 32 * kg : 32 * qh, f >> 1);
+                return (f & 1) ? tlk.row(sK, 0, f >> 1) : tlq.row(sQ, 0, f >> 1);
             };
             bf16x8 ring[PF];
 #pragma unroll
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         {
             constexpr int NF = 2 * NKS;                 // dO rows (A), V rows (B)
             auto frag = [&](int f) __attribute__((always_inline)) {
-                return tl.row((f & 1) ? sV : sG, (f & 1) ? 32 * kg : 32 * qh, f >> 1);
+                return (f & 1) ? tlk.row(sV, 0, f >> 1) : tlq.row(sG, 0, f >> 1);
             };
             bf16x8 ring[PF];
 #pragma unroll
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         {
             constexpr int NM = 2 * NDT;
             auto frag = [&](int m) __attribute__((always_inline)) {
-                return tl.tr(sG, 32 * qh + 16 * (m / NDT), m % NDT);
+                return tlq.tr(sG, 16 * (m / NDT), m % NDT);
             };
             bf16x8 ring[PF];
 #pragma unroll
@@ -589,7 +591,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         {
             constexpr int NM = 2 * NDT;
             auto frag = [&](int m) __attribute__((always_inline)) {
-                return tl.tr(sQ, 32 * qh + 16 * (m / NDT), m % NDT);
+                return tlq.tr(sQ, 16 * (m / NDT), m % NDT);
             };
             bf16x8 ring[PF];
 #pragma unroll

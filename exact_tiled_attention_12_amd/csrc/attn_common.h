@@ -185,27 +185,32 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, char* tile, i
 //     Within each group of 16 lanes, ds_read_b64_tr_b16 hands lane i element i%4
 //     of the reads of lanes 4k + i/4 (k = 0..3), so lane 16g + j reads row
 //     k0 + 4 (g/2) + j/4, columns 32 jt + 16 (g%2) + 4 (j%4) .. +3.
+//   init(lane, row0): every offset moved down by row0 rows (row0 a multiple of 16, so the
+//     swizzle is unchanged), for a wave that always reads from its own row band: the
+//     wave-uniform band then costs nothing per read, instead of an address register per
+//     (buffer, contraction step) pair.
 template <int RB, int NKS, int NJT, bool FAST>
 struct TileLane {
     int ro[NKS];
     int ta[FAST ? NJT : 2], tb[FAST ? NJT : 1];
-    __device__ __forceinline__ void init(int lane)
+    __device__ __forceinline__ void init(int lane, int row0 = 0)
     {
         const int l32 = lane & 31, h = lane >> 5;
+        const int band = row0 * RB;
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) ro[s] = l32 * RB + swz<RB, FAST>(l32, 2 * s + h) * 16;
+        for (int s = 0; s < NKS; ++s) ro[s] = band + l32 * RB + swz<RB, FAST>(l32, 2 * s + h) * 16;
         const int g = lane >> 4, j = lane & 15;
         const int rl = 4 * (g >> 1) + (j >> 2);            // row within the 8-row group
         const int cl = 16 * (g & 1) + 4 * (j & 3);         // column within the 32-column tile
         if constexpr (FAST) {
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) {
-                ta[jt] = tile_off<RB, FAST>(rl, 32 * jt + cl);
-                tb[jt] = tile_off<RB, FAST>(rl + 8, 32 * jt + cl);
+                ta[jt] = band + tile_off<RB, FAST>(rl, 32 * jt + cl);
+                tb[jt] = band + tile_off<RB, FAST>(rl + 8, 32 * jt + cl);
             }
         } else {
-            ta[0] = tile_off<RB, FAST>(rl, cl);
-            ta[1] = tile_off<RB, FAST>(rl, 32 + cl);
+            ta[0] = band + tile_off<RB, FAST>(rl, cl);
+            ta[1] = band + tile_off<RB, FAST>(rl, 32 + cl);
         }
     }
     __device__ __forceinline__ bf16x8 row(const char* tile, int m0, int s) const
