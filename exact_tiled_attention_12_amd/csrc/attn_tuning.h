@@ -24,7 +24,7 @@ struct TuneEntry {
 // ---- generated table: begin ----
 static constexpr TuneEntry kTuneTable[] = {
     {kTuneDkdv, 80, 1, 1 << 30, 32, 64},
-    {kTuneDkdv, 128, 1, 4096, 16, 64},
+    {kTuneDkdv, 128, 1, 4096, 32, 64},
     {kTuneDkdv, 128, 1, 1 << 30, 32, 64},
     {kTuneDq, 80, 1, 1 << 30, 64, 64},
     {kTuneDq, 128, 1, 4096, 128, 64},
