@@ -616,6 +616,7 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
     constexpr float NEG_INF = -__builtin_inff();
     __shared__ __attribute__((aligned(1024))) char sK0[C::T_BYTES], sK1[C::T_BYTES];
     __shared__ __attribute__((aligned(1024))) char sV0[C::T_BYTES], sV1[C::T_BYTES];
+    __shared__ __attribute__((aligned(256))) char sO[WAVES * 32 * RB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -632,18 +633,10 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
     TileLane<RB, NKS, NDT, true> tl;
     tl.init(lane);
 
-    // Q fragments (B operand of S^T = K Q^T), sign-flipped for a negative scale
-    bf16x8 qf[NKS];
-    {
-        const auto rq = make_rsrc(Q + hoff, (uint32_t)N * ROWB);
-        const uint32_t ro = (uint32_t)myq * ROWB + 16 * h;
-#pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            u32x4 raw = buf_ld16(rq, ro + 32 * s);
-            if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-            qf[s] = __builtin_bit_cast(bf16x8, raw);
-        }
-    }
+    // this wave's 32 query rows go to its own rows of sO (direct-to-LDS, whole rows per
+    // instruction); sO holds nothing else until the epilogue stages O there
+    dma_rows<D, RB, true>(make_rsrc(Q + hoff + (size_t)q0 * D, (uint32_t)(N - q0) * ROWB), sO, 32 * wave, 32, lane);
+    bf16x8 qf[NKS];                             // read from sO once the prologue's loads landed
 
     f32x16 oacc[NDT];
 #pragma unroll
@@ -712,6 +705,13 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
     if (ntiles > 1) issue(Kh, 1, sK1);
     wait_vmem_all();
     __syncthreads();
+    // Q fragments (B operand of S^T = K Q^T), sign-flipped for a negative scale
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        u32x4 raw = __builtin_bit_cast(u32x4, tl.row(sO, 32 * wave, s));
+        if (negate_q) raw ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        qf[s] = __builtin_bit_cast(bf16x8, raw);
+    }
     scores(sA, sK0, [&](int) {});
     {
         float mx4[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
@@ -821,25 +821,34 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
     }
     if (j < ntiles) step(j, sA, sB, sK1, sV0, sK0, sV1);
 
-    // epilogue: one division by l, O and LSE written once
+    // epilogue: one division by l; O goes through this wave's own LDS rows (swizzled like a
+    // K/V tile) so that every store instruction writes whole rows; LSE written once
     const float lt = l + xor32(l);
     const float inv = 1.0f / lt;
-    if (myq < N) {
-        bf16* dst = O + hoff + (size_t)myq * D;
+    {
+        char* st = sO + wave * 32 * RB;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * dt + 8 * g + 4 * h;
-                if (d0 < D) {
+                if (32 * dt + 8 * g < D) {
                     bf16x4 v;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = to_bf16(oacc[dt][4 * g + e] * inv);
-                    *reinterpret_cast<bf16x4*>(dst + d0) = v;
+                    *reinterpret_cast<bf16x4*>(st + l32 * RB + swz<RB, true>(l32, 4 * dt + g) * 16 + 8 * h) = v;
                 }
             }
-        if (h == 0) LSE[(size_t)head * N + myq] = (mc + __log2f(lt)) * kLn2;
+        constexpr int CPR = D / 8, NCH = 32 * CPR;
+        static_assert(NCH % 64 == 0, "whole store instructions");
+        const auto ro = make_rsrc(O + hoff + (size_t)q0w * D, (uint32_t)(N > q0w ? N - q0w : 0) * ROWB);
+#pragma unroll
+        for (int i = 0; i < NCH / 64; ++i) {
+            const int idx = 64 * i + lane, row = idx / CPR, ch = idx - row * CPR;
+            const u32x4 v = ld16(st + row * RB + swz<RB, true>(row, ch) * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, row * (int)ROWB + ch * 16, 0, 0);
+        }
     }
+    if (myq < N && h == 0) LSE[(size_t)head * N + myq] = (mc + __log2f(lt)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
