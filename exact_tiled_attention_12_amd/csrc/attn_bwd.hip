@@ -499,6 +499,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     // MFMA next to its slice of VALU work.
     auto block_body = [&](int i, const char* sQ, const char* sG, const float* sL, const float* sD) {
         const int q0 = i * C::BM;
+        // the two waves of a SIMD run the same block; priority 3, 2, 1, 0 over its four products
+        // gives the wave that is behind the issue slots (else the older wave always wins them,
+        // finishes first and idles at the next barrier while the other runs alone)
+        __builtin_amdgcn_s_setprio(3);
         constexpr int PF = 4, NKS = C::NKS, NDT = C::NDT;
         f32x16 sacc, pacc;
         {
@@ -520,6 +524,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        __builtin_amdgcn_s_setprio(2);
         {
             constexpr int NF = 2 * NKS;                 // dO rows (A), V rows (B)
             auto frag = [&](int f) __attribute__((always_inline)) {
@@ -560,6 +565,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = to_bf16(sacc[r]);
+        __builtin_amdgcn_s_setprio(1);
         // dV^T += dO^T P (products m = s2 * NDT + dt) while dS = P (dP - D) is computed
         {
             constexpr int NM = 2 * NDT;
@@ -587,6 +593,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // dK^T += Q^T dS
         {
             constexpr int NM = 2 * NDT;

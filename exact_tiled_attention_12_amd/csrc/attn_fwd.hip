@@ -763,6 +763,7 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
         // [A] the next tile's score MFMAs with the exponentials of keys 0-31
         scores(snext, sKn, [&](int i) __attribute__((always_inline)) {
             constexpr int NM = NKS * 2;
+            if (i == NM / 2) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
             for (int r = 16 * i / NM; r < 16 * (i + 1) / NM; ++r) {
                 expo(0, r);
@@ -785,6 +786,8 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
             if (t + PF < NT) ring[t % PF] = tfrag(t + PF);
             const int kt = t / (2 * NDT), s2 = (t / NDT) & 1, dt = t % NDT;
             oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][s2], oacc[dt], 0, 0, 0);
+            if (t == 0) __builtin_amdgcn_s_setprio(1);
+            if (t == 2 * NDT) __builtin_amdgcn_s_setprio(0);
             if (t < 2 * NDT) {
                 // [B1] keys 0-31 of P V, with the exponentials of keys 32-63
 #pragma unroll
@@ -809,6 +812,11 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
                     char* sVl) __attribute__((always_inline)) {
         wait_vmem_all();                            // this wave's loads of K_{j+1} and V_j landed
         __syncthreads();                            // everyone's; iteration j-1 fully read
+        // the two waves of a SIMD (w and w + 4) run the same step; by default the older one wins
+        // every issue contest, finishes first and idles at the next barrier while the other runs
+        // alone.  Priority 3, 2, 1, 0 at the quarters of the step gives the wave that is behind
+        // the issue slots instead.
+        __builtin_amdgcn_s_setprio(3);
         if (j + 2 < ntiles) issue(Kh, j + 2, sKl);
         if (j + 1 < ntiles) issue(Vh, j + 1, sVl);
         if (j <= jlast) body(j, scur, snext, sKn, sVc);
