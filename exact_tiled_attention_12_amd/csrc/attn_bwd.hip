@@ -497,7 +497,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     //   dV^T += dO^T P while dS = P o (dP - D) is computed;  dK^T += Q^T dS.
     // Fragments are read PF MFMAs ahead through small rings; sched_barrier keeps each
     // MFMA next to its slice of VALU work.
-    auto block_body = [&](int i, const char* sQ, const char* sG, const float* sL, const float* sD) {
+    // `loads` issues the next block's direct-to-LDS loads; it runs after the fourth score product,
+    // so that the step's loads do not all queue at the address unit while the waves wait
+    auto block_body = [&](int i, const char* sQ, const char* sG, const float* sL, const float* sD, auto&& loads) {
         const int q0 = i * C::BM;
         // the two waves of a SIMD run the same block; priority 3, 2, 1, 0 over its four products
         // gives the wave that is behind the issue slots (else the older wave always wins them,
@@ -507,6 +509,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         f32x16 sacc, pacc;
         {
             constexpr int NF = 2 * NKS;                 // f: s = f / 2; A (Q rows), then B (K rows)
+            static_assert(NF >= 8, "the loads go out after the fourth product");
             auto frag = [&](int f) __attribute__((always_inline)) {
                 return (f & 1) ? tlk.row(sK, 0, f >> 1) : tlq.row(sQ, 0, f >> 1);
             };
@@ -521,6 +524,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                     ring[(f + 1) % PF] = frag(f + PF + 1);
                 }
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, f == 0 ? f32x16{} : sacc, 0, 0, 0);
+                if (f == 6) loads();                      // NF >= 8 for every head dim
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -619,8 +623,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
             if (wave == 0) lc[lane] = lreg;
             if (wave == 1) dc[lane] = lreg;
             __syncthreads();                            // everyone's loads landed; block i-1 fully read
-            if (i + 1 < nq) issue_block(i + 1, qn, gn);
-            block_body(i, qc, gc, lc, dc);
+            block_body(i, qc, gc, lc, dc, [&]() __attribute__((always_inline)) {
+                if (i + 1 < nq) issue_block(i + 1, qn, gn);
+            });
         };
         issue_block(i0, sQ0, sG0);
         int i = i0;
@@ -636,8 +641,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
             if (wave == 0) lc[lane] = lreg;
             if (wave == 1) dc[lane] = lreg;
             __syncthreads();
-            if (in < nq) issue_block(in, qn, gn);
-            block_body(i, qc, gc, lc, dc);
+            block_body(i, qc, gc, lc, dc, [&]() __attribute__((always_inline)) {
+                if (in < nq) issue_block(in, qn, gn);
+            });
         };
         // only the query blocks of kept mask rows (two 64-query blocks per mask block);
         // this workgroup's keys are mask column kb

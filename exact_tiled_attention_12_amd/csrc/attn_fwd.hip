@@ -29,6 +29,8 @@
 // ones, with the same arithmetic.
 #include <float.h>
 
+#include <type_traits>
+
 #include "../../include/attn.h"
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -723,7 +725,9 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
     // One iteration: scur = S_j, snext <- S_{j+1}; sKn holds K_{j+1}, sVc V_j.  On a wave's last
     // tile, [A] still runs on whatever the K buffer holds (in bounds) and its result is never
     // used: a branch around it would make the compiler copy the live score tile at the join.
-    auto body = [&](int j, f32x16 (&scur)[2], f32x16 (&snext)[2], const char* sKn, const char* sVc)
+    // `sVl`: where V_{j+1} goes when this body issues it (after the second score product, so
+    // that the step's loads do not all queue at the address unit at once), else null
+    auto body = [&](int j, f32x16 (&scur)[2], f32x16 (&snext)[2], const char* sKn, const char* sVc, char* sVl)
         __attribute__((always_inline)) {
         // tiles crossing the diagonal or N (rare): mask S_j in place and take its max again
         float mxc = mxc_next;
@@ -763,6 +767,7 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
         // [A] the next tile's score MFMAs with the exponentials of keys 0-31
         scores(snext, sKn, [&](int i) __attribute__((always_inline)) {
             constexpr int NM = NKS * 2;
+            if (i == 2 && sVl != nullptr && j + 1 < ntiles) issue(Vh, j + 1, sVl);
             if (i == NM / 2) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
             for (int r = 16 * i / NM; r < 16 * (i + 1) / NM; ++r) {
@@ -808,8 +813,10 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
         l += ls[0] + ls[1];
     };
 
-    auto step = [&](int j, f32x16 (&scur)[2], f32x16 (&snext)[2], const char* sKn, const char* sVc, char* sKl,
-                    char* sVl) __attribute__((always_inline)) {
+    // ALL: a step in which every wave of the workgroup has a tile (all but a causal block's last
+    // three), so no wave skips the body and the body issues V; else V is issued here
+    auto step = [&](auto all, int j, f32x16 (&scur)[2], f32x16 (&snext)[2], const char* sKn, const char* sVc,
+                    char* sKl, char* sVl) __attribute__((always_inline)) {
         wait_vmem_all();                            // this wave's loads of K_{j+1} and V_j landed
         __syncthreads();                            // everyone's; iteration j-1 fully read
         // the two waves of a SIMD (w and w + 4) run the same step; by default the older one wins
@@ -818,16 +825,27 @@ void fwd_kernel_bf16_pipe(const bf16* __restrict__ Q, const bf16* __restrict__ K
         // the issue slots instead.
         __builtin_amdgcn_s_setprio(3);
         if (j + 2 < ntiles) issue(Kh, j + 2, sKl);
-        if (j + 1 < ntiles) issue(Vh, j + 1, sVl);
-        if (j <= jlast) body(j, scur, snext, sKn, sVc);
+        if constexpr (decltype(all)::value) {
+            body(j, scur, snext, sKn, sVc, sVl);
+        } else {
+            if (j + 1 < ntiles) issue(Vh, j + 1, sVl);
+            if (j <= jlast) body(j, scur, snext, sKn, sVc, nullptr);
+        }
     };
     // even j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1 (odd j mirrored)
+    const int jbusy = CAUSAL ? min(ntiles, (q0 + 31) / C::BN + 1) : ntiles;    // wave 0's last tile + 1
+    const std::integral_constant<bool, true> all_busy;
+    const std::integral_constant<bool, false> some_idle;
     int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        step(j, sA, sB, sK1, sV0, sK0, sV1);
-        step(j + 1, sB, sA, sK0, sV1, sK1, sV0);
+    for (; j + 1 < jbusy; j += 2) {
+        step(all_busy, j, sA, sB, sK1, sV0, sK0, sV1);
+        step(all_busy, j + 1, sB, sA, sK0, sV1, sK1, sV0);
     }
-    if (j < ntiles) step(j, sA, sB, sK1, sV0, sK0, sV1);
+    for (; j + 1 < ntiles; j += 2) {
+        step(some_idle, j, sA, sB, sK1, sV0, sK0, sV1);
+        step(some_idle, j + 1, sB, sA, sK0, sV1, sK1, sV0);
+    }
+    if (j < ntiles) step(some_idle, j, sA, sB, sK1, sV0, sK0, sV1);
 
     // epilogue: one division by l; O goes through this wave's own LDS rows (swizzled like a
     // K/V tile) so that every store instruction writes whole rows; LSE written once
