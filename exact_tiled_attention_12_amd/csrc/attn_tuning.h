@@ -29,13 +29,13 @@ static constexpr TuneEntry kTuneTable[] = {
     {kTuneDq, 80, 1, 1 << 30, 64, 64},
     {kTuneDq, 128, 1, 4096, 128, 64},
     {kTuneDq, 128, 1, 1 << 30, 64, 64},
-    {kTuneFwdBf16, 80, 1, 1 << 30, 32, 64},
+    {kTuneFwdBf16, 80, 1, 1 << 30, 64, 64},
     {kTuneFwdBf16, 128, 1, 4096, 64, 64},
-    {kTuneFwdBf16, 128, 1, 1 << 30, 128, 64},
+    {kTuneFwdBf16, 128, 1, 1 << 30, 64, 64},
     {kTuneFwdFp8, 64, 0, 1 << 30, 64, 64},
     {kTuneFwdFp8, 128, 0, 1 << 30, 64, 64},
-    {kTuneFwdFp8, 128, 1, 4096, 64, 64},
-    {kTuneFwdFp8, 128, 1, 1 << 30, 32, 128},
+    {kTuneFwdFp8, 128, 1, 4096, 128, 64},
+    {kTuneFwdFp8, 128, 1, 1 << 30, 128, 128},
     {kTuneFwdBf16, 0, 1, 1 << 30, 64, 64},
     {kTuneDkdv, 0, 1, 1 << 30, 32, 64},
     {kTuneDq, 0, 1, 1 << 30, 64, 64},
