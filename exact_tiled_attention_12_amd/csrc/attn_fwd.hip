@@ -591,8 +591,8 @@ void fwd_kernel_bf16_sparse(const bf16* __restrict__ Q, const bf16* __restrict__
 }
 
 // ----------------------------------------------------------------------------
-// bf16 forward, dense walks: the same arithmetic as fwd_kernel_bf16 (same products in
-// the same order, same roundings, same rescale decisions: bit-identical results),
+// bf16 forward, dense walks: the same arithmetic as fwd_kernel_bf16_sparse (same products
+// in the same order, same roundings, same rescale decisions: bit-identical results),
 // software-pipelined across key tiles so that each wave's softmax runs under its own
 // MFMAs instead of between them.  Iteration j of a wave:
 //   [A]  S_{j+1} = K_{j+1} Q^T   (16 MFMAs at d = 128)  with  exp2 of S_j, keys 0-31
@@ -600,8 +600,14 @@ void fwd_kernel_bf16_sparse(const bf16* __restrict__ Q, const bf16* __restrict__
 //   [B2] O^T += V_j^T P_j^T, keys 32-63                  with  the row max of S_{j+1}
 // and the rare rescale of O and l (lazy, threshold 2^8) at the top, before the
 // exponentials of S_j need the reference max.  K runs one tile ahead of V: at the top
-// of iteration j (one barrier) K_{j+2} and V_{j+1} are issued into the buffers that
-// iteration j-1 finished reading, and iteration j reads K_{j+1} and V_j.
+// of iteration j (one barrier) K_{j+2} is issued, and V_{j+1} after the second score
+// product (so that the step's direct-to-LDS loads do not all queue at the address unit
+// at once), into the buffers that iteration j-1 finished reading; iteration j reads
+// K_{j+1} and V_j.  A causal block's last three iterations, where some waves have no
+// tile, run in a loop of their own with both loads at the top.  Wave priority steps
+// 3, 2, 1, 0 through each iteration so that the two waves of a SIMD finish together.
+// Q comes in and O goes out through each wave's own rows of an LDS stage, so that every
+// global load and store instruction moves whole rows.
 // 8 waves (256 query rows) per workgroup, 32 rows per wave, two waves per SIMD.
 // ----------------------------------------------------------------------------
 template <int D, bool CAUSAL>
