@@ -668,7 +668,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     // and the row reads are free of bank conflicts), key group g's rows in the g-th Q/dO
     // buffer: dV first, then dK.  After each sum all eight waves store whole rows, so each
     // store instruction writes contiguous memory.  The K/V tiles are free from the start of
-    // the epilogue, so the next item's K and V rows are issued first and load meanwhile.
+    // the epilogue, so the next item's K and V rows are issued first and load during the
+    // sums: the sums' barriers order LDS only (lds_barrier), and every staging access names
+    // its Q/dO buffer directly, so that the compiler sees it apart from the K/V tiles being
+    // loaded (through a pointer chosen per wave it cannot, and would wait for those loads).
     wait_vmem_all();
     __syncthreads();                                    // every tile fully read
     {
@@ -683,9 +686,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         constexpr int NCHP = C::DP / 4 <= 16 ? 16 : 32;  // 16-byte chunks per LDS row (power of two)
         constexpr int GROUP_BYTES = 32 * NCHP * 16;      // one key group's rows
         static_assert(GROUP_BYTES <= C::Q_BYTES, "epilogue staging fits");
-        auto kbuf = [&](int g) -> char* { return g == 0 ? sQ0 : g == 1 ? sQ1 : g == 2 ? sG0 : sG1; };
         auto soff = [](int row, int ch) { return (row * NCHP + (ch ^ (row & 15))) * 16; };
-        char* kb = kbuf(kg);
         // lane index made opaque here, so that the offsets below are computed per item and
         // not hoisted out of the item loop (where they would sit in registers the main loop needs)
         int lane_e = lane;
@@ -693,50 +694,74 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         const int l32e = lane_e & 31, he = lane_e >> 5, tid_e = 64 * wave + lane_e;
         auto sum_store = [&](const f32x16 (&acc)[C::NDT], G* __restrict__ dst, float mult) {
             // lane: key row l32 of the group; accumulator rows d = 32 dt + 8 g4 + 4 h + e -> chunk 8 dt + 2 g4 + h
-            if (qh == 0) {
+            auto put = [&](char* buf) __attribute__((always_inline)) {
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4)
-                        *reinterpret_cast<f32x4*>(kb + soff(l32e, 8 * dt + 2 * g4 + he)) =
+                        *reinterpret_cast<f32x4*>(buf + soff(l32e, 8 * dt + 2 * g4 + he)) =
                             f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
-            }
-            __syncthreads();
-            if (qh == 1) {
+            };
+            auto add = [&](char* buf) __attribute__((always_inline)) {
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
                         const int o = soff(l32e, 8 * dt + 2 * g4 + he);
-                        f32x4 pk = *reinterpret_cast<const f32x4*>(kb + o);
+                        f32x4 pk = *reinterpret_cast<const f32x4*>(buf + o);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) pk[e] += acc[dt][4 * g4 + e];
-                        *reinterpret_cast<f32x4*>(kb + o) = pk;
+                        *reinterpret_cast<f32x4*>(buf + o) = pk;
                     }
+            };
+            // one branch per key group, each naming its buffer; the distinct empty asm
+            // statements keep the compiler from merging the four into one access through
+            // a selected pointer
+            if (qh == 0) {
+                if (kg == 0) { asm volatile("; put 0"); put(sQ0); asm volatile("; put 0 end"); }
+                if (kg == 1) { asm volatile("; put 1"); put(sQ1); asm volatile("; put 1 end"); }
+                if (kg == 2) { asm volatile("; put 2"); put(sG0); asm volatile("; put 2 end"); }
+                if (kg == 3) { asm volatile("; put 3"); put(sG1); asm volatile("; put 3 end"); }
             }
-            __syncthreads();
-            // D/4 chunks per key row, consecutive threads take consecutive chunks of a row
-            constexpr int CPR = D / 4, TOTAL = C::BN * CPR, THREADS = 64 * C::WAVES;
-            static_assert(TOTAL % THREADS == 0, "whole passes");
+            lds_barrier();
+            if (qh == 1) {
+                if (kg == 0) { asm volatile("; add 0"); add(sQ0); asm volatile("; add 0 end"); }
+                if (kg == 1) { asm volatile("; add 1"); add(sQ1); asm volatile("; add 1 end"); }
+                if (kg == 2) { asm volatile("; add 2"); add(sG0); asm volatile("; add 2 end"); }
+                if (kg == 3) { asm volatile("; add 3"); add(sG1); asm volatile("; add 3 end"); }
+            }
+            lds_barrier();
+            // group by group, D/4 chunks per key row, consecutive threads take consecutive
+            // chunks of a row
+            constexpr int CPR = D / 4, GTOTAL = 32 * CPR, THREADS = 64 * C::WAVES;
+            constexpr int PASSES = (GTOTAL + THREADS - 1) / THREADS;
+            auto rows = [&](const char* buf, int g) __attribute__((always_inline)) {
 #pragma unroll
-            for (int pass = 0; pass < TOTAL / THREADS; ++pass) {
-                const int c = pass * THREADS + tid_e;
-                const int row = c / CPR, ch = c - row * CPR;
-                const int key = k0 + row;
-                const f32x4 a = *reinterpret_cast<const f32x4*>(kbuf(row >> 5) + soff(row & 31, ch));
-                if (key < N) {
-                    G* pk = dst + hoff + (size_t)key * D + 4 * ch;
-                    if constexpr (sizeof(G) == 4) {
-                        *reinterpret_cast<f32x4*>(pk) = a * mult;
-                    } else {
-                        bf16x4 x;
+                for (int pass = 0; pass < PASSES; ++pass) {
+                    const int c = pass * THREADS + tid_e;
+                    if (GTOTAL % THREADS == 0 || c < GTOTAL) {
+                        const int row = c / CPR, ch = c - row * CPR;
+                        const int key = k0 + 32 * g + row;
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(buf + soff(row, ch));
+                        if (key < N) {
+                            G* pk = dst + hoff + (size_t)key * D + 4 * ch;
+                            if constexpr (sizeof(G) == 4) {
+                                *reinterpret_cast<f32x4*>(pk) = a * mult;
+                            } else {
+                                bf16x4 x;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = to_bf16(a[e] * mult);
-                        *reinterpret_cast<bf16x4*>(pk) = x;
+                                for (int e = 0; e < 4; ++e) x[e] = to_bf16(a[e] * mult);
+                                *reinterpret_cast<bf16x4*>(pk) = x;
+                            }
+                        }
                     }
                 }
-            }
-            __syncthreads();                            // the staging rows are read
+            };
+            rows(sQ0, 0);
+            rows(sQ1, 1);
+            rows(sG0, 2);
+            rows(sG1, 3);
+            lds_barrier();                               // the staging rows are read
         };
         sum_store(dvacc, dV, 1.0f);                     // dV = (dV^T acc)^T
         sum_store(dkacc, dK, scale);                    // dK = scale * (dK^T acc)^T

@@ -240,6 +240,20 @@ struct TileLane {
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier over LDS only: this wave's LDS operations complete (lgkmcnt(0)),
+// then s_barrier.  __syncthreads() releases with a fence that also waits for every
+// direct-to-LDS load in flight (those write LDS); here such loads, and global stores,
+// stay in flight, so the LDS they target must not be read before a wait_vmem_all()
+// and a barrier.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0); vmcnt, expcnt unconstrained
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // s_waitcnt vmcnt(n) (other counters left unconstrained), n <= 63: waits until at
 // most n vector-memory instructions of this wave are outstanding.
 __device__ __forceinline__ void wait_vmem_leave(int n)
