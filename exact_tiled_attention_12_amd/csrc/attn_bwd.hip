@@ -699,14 +699,16 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4)
-                        *reinterpret_cast<f32x4*>(buf + soff(l32e, 8 * dt + 2 * g4 + he)) =
-                            f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
+                        if (32 * dt + 8 * g4 < D)       // rows d >= D are padding (d = 80)
+                            *reinterpret_cast<f32x4*>(buf + soff(l32e, 8 * dt + 2 * g4 + he)) =
+                                f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
             };
             auto add = [&](char* buf) __attribute__((always_inline)) {
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
+                        if (32 * dt + 8 * g4 >= D) continue;
                         const int o = soff(l32e, 8 * dt + 2 * g4 + he);
                         f32x4 pk = *reinterpret_cast<const f32x4*>(buf + o);
 #pragma unroll
@@ -731,36 +733,36 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                 if (kg == 3) { asm volatile("; add 3"); add(sG1); asm volatile("; add 3 end"); }
             }
             lds_barrier();
-            // group by group, D/4 chunks per key row, consecutive threads take consecutive
-            // chunks of a row
-            constexpr int CPR = D / 4, GTOTAL = 32 * CPR, THREADS = 64 * C::WAVES;
-            constexpr int PASSES = (GTOTAL + THREADS - 1) / THREADS;
+            // waves 2g and 2g + 1 store group g's rows: D/4 chunks per key row, consecutive threads
+            // take consecutive chunks of a row
+            constexpr int CPR = D / 4, GTOTAL = 32 * CPR, GTHREADS = 128;
+            static_assert(GTOTAL % GTHREADS == 0, "whole passes");
+            const int gt = tid_e & (GTHREADS - 1);
             auto rows = [&](const char* buf, int g) __attribute__((always_inline)) {
 #pragma unroll
-                for (int pass = 0; pass < PASSES; ++pass) {
-                    const int c = pass * THREADS + tid_e;
-                    if (GTOTAL % THREADS == 0 || c < GTOTAL) {
-                        const int row = c / CPR, ch = c - row * CPR;
-                        const int key = k0 + 32 * g + row;
-                        const f32x4 a = *reinterpret_cast<const f32x4*>(buf + soff(row, ch));
-                        if (key < N) {
-                            G* pk = dst + hoff + (size_t)key * D + 4 * ch;
-                            if constexpr (sizeof(G) == 4) {
-                                *reinterpret_cast<f32x4*>(pk) = a * mult;
-                            } else {
-                                bf16x4 x;
+                for (int pass = 0; pass < GTOTAL / GTHREADS; ++pass) {
+                    const int c = pass * GTHREADS + gt;
+                    const int row = c / CPR, ch = c - row * CPR;
+                    const int key = k0 + 32 * g + row;
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(buf + soff(row, ch));
+                    if (key < N) {
+                        G* pk = dst + hoff + (size_t)key * D + 4 * ch;
+                        if constexpr (sizeof(G) == 4) {
+                            *reinterpret_cast<f32x4*>(pk) = a * mult;
+                        } else {
+                            bf16x4 x;
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) x[e] = to_bf16(a[e] * mult);
-                                *reinterpret_cast<bf16x4*>(pk) = x;
-                            }
+                            for (int e = 0; e < 4; ++e) x[e] = to_bf16(a[e] * mult);
+                            *reinterpret_cast<bf16x4*>(pk) = x;
                         }
                     }
                 }
             };
-            rows(sQ0, 0);
-            rows(sQ1, 1);
-            rows(sG0, 2);
-            rows(sG1, 3);
+            const int wg2 = wave >> 1;
+            if (wg2 == 0) { asm volatile("; rows 0"); rows(sQ0, 0); asm volatile("; rows 0 end"); }
+            if (wg2 == 1) { asm volatile("; rows 1"); rows(sQ1, 1); asm volatile("; rows 1 end"); }
+            if (wg2 == 2) { asm volatile("; rows 2"); rows(sG0, 2); asm volatile("; rows 2 end"); }
+            if (wg2 == 3) { asm volatile("; rows 3"); rows(sG1, 3); asm volatile("; rows 3 end"); }
             lds_barrier();                               // the staging rows are read
         };
         sum_store(dvacc, dV, 1.0f);                     // dV = (dV^T acc)^T
