@@ -487,8 +487,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         const uint32_t bytes = (uint32_t)(N - q0) * ROWB;         // rows past N read as zeros
         dma_rows<D, RB, false>(make_rsrc(Qh + (size_t)q0 * D, bytes), sQ, wave * (C::BM / 8), C::BM / 8, lane);
         dma_rows<D, RB, false>(make_rsrc(dOh + (size_t)q0 * D, bytes), sG, wave * (C::BM / 8), C::BM / 8, lane);
-        if (wave == 0)
-            lreg = -kLog2e * buf_ld4f(make_rsrc(LSE + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
+        // raw values: scaling here would make wave 0 wait for every load in flight, the block's
+        // Q/dO rows included, right after issuing them (the step top scales LSE after its wait)
+        if (wave == 0) lreg = buf_ld4f(make_rsrc(LSE + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
         if (wave == 1) lreg = buf_ld4f(make_rsrc(Dg + (size_t)head * N + q0, (uint32_t)(N - q0) * 4), lane * 4);
     };
 
@@ -620,7 +621,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     if constexpr (!SPARSE) {
         auto step = [&](int i, char* qc, char* gc, float* lc, float* dc, char* qn, char* gn) {
             wait_vmem_all();                            // this wave's loads of block i landed
-            if (wave == 0) lc[lane] = lreg;
+            if (wave == 0) lc[lane] = -kLog2e * lreg;
             if (wave == 1) dc[lane] = lreg;
             __syncthreads();                            // everyone's loads landed; block i-1 fully read
             block_body(i, qc, gc, lc, dc, [&]() __attribute__((always_inline)) {
@@ -638,7 +639,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         // in: the next query block to visit (nq if none)
         auto step = [&](int i, int in, char* qc, char* gc, float* lc, float* dc, char* qn, char* gn) {
             wait_vmem_all();
-            if (wave == 0) lc[lane] = lreg;
+            if (wave == 0) lc[lane] = -kLog2e * lreg;
             if (wave == 1) dc[lane] = lreg;
             __syncthreads();
             block_body(i, qc, gc, lc, dc, [&]() __attribute__((always_inline)) {
