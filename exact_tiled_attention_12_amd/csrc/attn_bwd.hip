@@ -667,12 +667,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     // Epilogue.  The two query halves' partials are summed in LDS, row-major (one key per
     // row, DP floats, 16-byte chunks XOR-swizzled by the row so that the MFMA-layout writes
     // and the row reads are free of bank conflicts), key group g's rows in the g-th Q/dO
-    // buffer: dV first, then dK.  After each sum all eight waves store whole rows, so each
-    // store instruction writes contiguous memory.  The K/V tiles are free from the start of
-    // the epilogue, so the next item's K and V rows are issued first and load during the
-    // sums: the sums' barriers order LDS only (lds_barrier), and every staging access names
-    // its Q/dO buffer directly, so that the compiler sees it apart from the K/V tiles being
-    // loaded (through a pointer chosen per wave it cannot, and would wait for those loads).
+    // buffer: dV first, then dK.  The first query half puts its partials there, the second
+    // adds its own, then waves 2g and 2g + 1 store group g's rows, so each store instruction
+    // writes contiguous memory.  The K/V tiles are free from the start of the epilogue: the
+    // first half issues the next item's K and V rows once its dV partials are put, so their
+    // address work overlaps the second half's adds, and they load during the sums.  The sums'
+    // barriers order LDS only (lds_barrier), and every staging access names its Q/dO buffer
+    // directly, so that the compiler sees it apart from the K/V tiles being loaded (through a
+    // pointer chosen per wave it cannot, and would wait for those loads).
     wait_vmem_all();
     __syncthreads();                                    // every tile fully read
     {
@@ -693,29 +695,36 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         int lane_e = lane;
         asm volatile("" : "+v"(lane_e));
         const int l32e = lane_e & 31, he = lane_e >> 5, tid_e = 64 * wave + lane_e;
-        auto sum_store = [&](const f32x16 (&acc)[C::NDT], G* __restrict__ dst, float mult) {
+        auto sum_store = [&](const f32x16 (&acc)[C::NDT], G* __restrict__ dst, float mult, auto&& after_put) {
             // lane: key row l32 of the group; accumulator rows d = 32 dt + 8 g4 + 4 h + e -> chunk 8 dt + 2 g4 + h
+            // (rows d >= D are padding, d = 80)
             auto put = [&](char* buf) __attribute__((always_inline)) {
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4)
-                        if (32 * dt + 8 * g4 < D)       // rows d >= D are padding (d = 80)
+                        if (32 * dt + 8 * g4 < D)
                             *reinterpret_cast<f32x4*>(buf + soff(l32e, 8 * dt + 2 * g4 + he)) =
                                 f32x4{acc[dt][4 * g4], acc[dt][4 * g4 + 1], acc[dt][4 * g4 + 2], acc[dt][4 * g4 + 3]};
             };
+            // every partial read before the first write, so that the reads are in flight together
             auto add = [&](char* buf) __attribute__((always_inline)) {
+                f32x4 pk[C::NDT * 4];
 #pragma unroll
                 for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        if (32 * dt + 8 * g4 >= D) continue;
-                        const int o = soff(l32e, 8 * dt + 2 * g4 + he);
-                        f32x4 pk = *reinterpret_cast<const f32x4*>(buf + o);
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        if (32 * dt + 8 * g4 < D)
+                            pk[4 * dt + g4] = *reinterpret_cast<const f32x4*>(buf + soff(l32e, 8 * dt + 2 * g4 + he));
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pk[e] += acc[dt][4 * g4 + e];
-                        *reinterpret_cast<f32x4*>(buf + o) = pk;
-                    }
+                for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        if (32 * dt + 8 * g4 < D) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) pk[4 * dt + g4][e] += acc[dt][4 * g4 + e];
+                            *reinterpret_cast<f32x4*>(buf + soff(l32e, 8 * dt + 2 * g4 + he)) = pk[4 * dt + g4];
+                        }
             };
             // one branch per key group, each naming its buffer; the distinct empty asm
             // statements keep the compiler from merging the four into one access through
@@ -727,6 +736,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                 if (kg == 3) { asm volatile("; put 3"); put(sG1); asm volatile("; put 3 end"); }
             }
             lds_barrier();
+            if (qh == 0) after_put();
             if (qh == 1) {
                 if (kg == 0) { asm volatile("; add 0"); add(sQ0); asm volatile("; add 0 end"); }
                 if (kg == 1) { asm volatile("; add 1"); add(sQ1); asm volatile("; add 1 end"); }
@@ -735,27 +745,33 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
             }
             lds_barrier();
             // waves 2g and 2g + 1 store group g's rows: D/4 chunks per key row, consecutive threads
-            // take consecutive chunks of a row
-            constexpr int CPR = D / 4, GTOTAL = 32 * CPR, GTHREADS = 128;
+            // take consecutive chunks of a row.  The stores are range-checked (rows past N fall
+            // outside the buffer and are dropped), so no pass branches and the group's LDS reads
+            // all issue before its first store.
+            constexpr int CPR = D / 4, GTOTAL = 32 * CPR, GTHREADS = 128, NPASS = GTOTAL / GTHREADS;
             static_assert(GTOTAL % GTHREADS == 0, "whole passes");
             const int gt = tid_e & (GTHREADS - 1);
+            const auto ro = make_rsrc(dst + hoff + (size_t)k0 * D, (uint32_t)(N - k0) * (uint32_t)(D * sizeof(G)));
             auto rows = [&](const char* buf, int g) __attribute__((always_inline)) {
+                f32x4 a[NPASS];
 #pragma unroll
-                for (int pass = 0; pass < GTOTAL / GTHREADS; ++pass) {
+                for (int pass = 0; pass < NPASS; ++pass) {
                     const int c = pass * GTHREADS + gt;
                     const int row = c / CPR, ch = c - row * CPR;
-                    const int key = k0 + 32 * g + row;
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(buf + soff(row, ch));
-                    if (key < N) {
-                        G* pk = dst + hoff + (size_t)key * D + 4 * ch;
-                        if constexpr (sizeof(G) == 4) {
-                            *reinterpret_cast<f32x4*>(pk) = a * mult;
-                        } else {
-                            bf16x4 x;
+                    a[pass] = *reinterpret_cast<const f32x4*>(buf + soff(row, ch));
+                }
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) x[e] = to_bf16(a[e] * mult);
-                            *reinterpret_cast<bf16x4*>(pk) = x;
-                        }
+                for (int pass = 0; pass < NPASS; ++pass) {
+                    const int c = pass * GTHREADS + gt;
+                    const int row = c / CPR, ch = c - row * CPR;
+                    const int off = ((32 * g + row) * D + 4 * ch) * (int)sizeof(G);
+                    if constexpr (sizeof(G) == 4) {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a[pass] * mult), ro, off, 0, 0);
+                    } else {
+                        bf16x4 x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = to_bf16(a[pass][e] * mult);
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), ro, off, 0, 0);
                     }
                 }
             };
@@ -766,8 +782,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
             if (wg2 == 3) { asm volatile("; rows 3"); rows(sG1, 3); asm volatile("; rows 3 end"); }
             lds_barrier();                               // the staging rows are read
         };
-        sum_store(dvacc, dV, 1.0f);                     // dV = (dV^T acc)^T
-        sum_store(dkacc, dK, scale);                    // dK = scale * (dK^T acc)^T
+        sum_store(dvacc, dV, 1.0f, []() {});            // dV = (dV^T acc)^T
+        sum_store(dkacc, dK, scale, []() {});           // dK = scale * (dK^T acc)^T
     }
     }
 }
