@@ -336,9 +336,9 @@ __host__ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
 // The query-side grids are dispatched by the hardware: an XCD hands its workgroups out
 // in order, consecutive ones to its four shader engines in turn, and waits for a free
 // CU in the engine whose turn it is (measured: four consecutive workgroups start
-// together, once the slowest of the four before them has finished).  So there G is at
-// least four (or all of the XCD's heads), which makes four consecutive workgroups four
-// heads' blocks of equal cost (with whole XCD rows; without them consecutive
+// together, once the slowest of the four before them has finished).  So there G is a
+// multiple of four (or all of the XCD's heads), which makes every four consecutive
+// workgroups four heads' blocks of equal cost (with whole XCD rows; without them consecutive
 // workgroups go to different XCDs).  The key side walks its items itself and keeps G.
 // (`slots` comes from the launch-parameter table of attn_tuning.h.)
 template <bool CAUSAL, bool HEAVY_LAST>
@@ -356,7 +356,8 @@ __host__ __device__ __forceinline__ void block_coords(int bid, int nb, int nblk,
         const int x = split ? (bid & 7) : 0;
         const int slots = split ? SLOTS : 8 * SLOTS;
         const int G0 = hx < (slots + nblk - 1) / nblk ? hx : (slots + nblk - 1) / nblk;
-        const int G = HEAVY_LAST && split && G0 < 4 ? (hx < 4 ? hx : 4) : G0;
+        const int G4 = (G0 + 3) & ~3;                   // G0 rounded up to whole shader-engine rounds
+        const int G = HEAVY_LAST && split ? (hx < G4 ? hx : G4) : G0;
         const int g = k / (G * nblk);
         const int gh = G < hx - g * G ? G : hx - g * G; // heads in this group
         const int kk = k - g * G * nblk;

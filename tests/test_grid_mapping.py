@@ -91,3 +91,38 @@ def test_key_side_walk_bijective(walk, BH, N, causal, ncu):
     for slots in SLOTS:
         head, blk = _coords(walk, causal, False, nitems, nkblk, slots)
         _assert_bijection(head, blk, BH, nkblk, f"dkdv BH={BH} N={N} causal={causal} slots={slots}")
+
+
+@pytest.mark.parametrize("BH,N", [(64, 4096), (16, 16384), (256, 2048), (128, 1024), (32, 8192), (8, 4096),
+                                  (64, 2816), (128, 2600), (48, 3000), (96, 1500)])
+def test_query_side_groups_fill_shader_engine_rounds(walk, BH, N):
+    """An XCD dispatches its workgroups in order, consecutive ones to its four shader engines in
+    turn, so block_coords gives the causal query-side grids a multiple of four heads per group:
+    every four consecutive workgroups of an XCD then hold blocks of one index (equal cost), or,
+    with fewer heads left in a group, each of them before the next index."""
+    for name, rows, heavy_last in GRIDS:
+        if not heavy_last:
+            continue
+        nblk = (N + rows - 1) // rows
+        hx = BH // 8
+        for slots in SLOTS:
+            head, blk = _coords(walk, True, True, BH * nblk, nblk, slots)
+            for x in range(8):
+                h, b = head[x::8], blk[x::8]            # XCD x's sequence
+                assert np.all(h // hx == x), f"{name} BH={BH} N={N} slots={slots}: heads leave XCD {x}"
+                # groups of G heads (a multiple of 4, or all of the XCD's), the last one possibly smaller;
+                # each group's positions run rank by rank over its heads
+                p = 0
+                while p < len(b):
+                    # the group's heads: the positions before the block index changes
+                    q = p
+                    while q < len(b) and b[q] == b[p]:
+                        q += 1
+                    gh = q - p
+                    assert gh == hx or gh % 4 == 0 or p + gh * nblk == len(b), \
+                        f"{name} BH={BH} N={N} slots={slots} XCD {x}: group of {gh} heads at {p}"
+                    for r in range(nblk):                                  # rank r: one index, gh heads
+                        seg = slice(p + r * gh, p + (r + 1) * gh)
+                        assert len(set(b[seg].tolist())) == 1 and len(set(h[seg].tolist())) == gh, \
+                            f"{name} BH={BH} N={N} slots={slots} XCD {x} rank {r} at {p}"
+                    p += gh * nblk
