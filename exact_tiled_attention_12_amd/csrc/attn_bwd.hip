@@ -669,9 +669,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
     // and the row reads are free of bank conflicts), key group g's rows in the g-th Q/dO
     // buffer: dV first, then dK.  The first query half puts its partials there, the second
     // adds its own, then waves 2g and 2g + 1 store group g's rows, so each store instruction
-    // writes contiguous memory.  The K/V tiles are free from the start of the epilogue: the
-    // first half issues the next item's K and V rows once its dV partials are put, so their
-    // address work overlaps the second half's adds, and they load during the sums.  The sums'
+    // writes contiguous memory.  The K/V tiles are free from the start of the epilogue, so
+    // the next item's K and V rows are issued first and load during the sums.  The sums'
     // barriers order LDS only (lds_barrier), and every staging access names its Q/dO buffer
     // directly, so that the compiler sees it apart from the K/V tiles being loaded (through a
     // pointer chosen per wave it cannot, and would wait for those loads).
@@ -695,7 +694,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
         int lane_e = lane;
         asm volatile("" : "+v"(lane_e));
         const int l32e = lane_e & 31, he = lane_e >> 5, tid_e = 64 * wave + lane_e;
-        auto sum_store = [&](const f32x16 (&acc)[C::NDT], G* __restrict__ dst, float mult, auto&& after_put) {
+        auto sum_store = [&](const f32x16 (&acc)[C::NDT], G* __restrict__ dst, float mult) {
             // lane: key row l32 of the group; accumulator rows d = 32 dt + 8 g4 + 4 h + e -> chunk 8 dt + 2 g4 + h
             // (rows d >= D are padding, d = 80)
             auto put = [&](char* buf) __attribute__((always_inline)) {
@@ -736,7 +735,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
                 if (kg == 3) { asm volatile("; put 3"); put(sG1); asm volatile("; put 3 end"); }
             }
             lds_barrier();
-            if (qh == 0) after_put();
             if (qh == 1) {
                 if (kg == 0) { asm volatile("; add 0"); add(sQ0); asm volatile("; add 0 end"); }
                 if (kg == 1) { asm volatile("; add 1"); add(sQ1); asm volatile("; add 1 end"); }
@@ -782,8 +780,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_bf16(const bf16* __restrict__ Q,
             if (wg2 == 3) { asm volatile("; rows 3"); rows(sG1, 3); asm volatile("; rows 3 end"); }
             lds_barrier();                               // the staging rows are read
         };
-        sum_store(dvacc, dV, 1.0f, []() {});            // dV = (dV^T acc)^T
-        sum_store(dkacc, dK, scale, []() {});           // dK = scale * (dK^T acc)^T
+        sum_store(dvacc, dV, 1.0f);                     // dV = (dV^T acc)^T
+        sum_store(dkacc, dK, scale);                    // dK = scale * (dK^T acc)^T
     }
     }
 }
