@@ -233,6 +233,53 @@ def workload_entry(idx, dev, steps, warmup):
     return ent
 
 
+def mfma_ceiling(dev, launches=20, iters=4096):
+    """What the matrix cores sustain now: libmfma_rate.so's pure bf16 MFMA loop (two waves per SIMD,
+    four independent accumulator chains per wave) over every CU, after ~50 ms of the same load so that
+    the clock has settled.  Returns its TFLOP/s (HIP events over `launches` launches), the shader clock
+    from its s_memtime / s_memrealtime stamps (median over workgroups, MHz), and the FLOP per CU and
+    clock those two imply (4096 when the products issue back to back), or None without the probe."""
+    import ctypes
+    import statistics
+    from exact_tiled_attention_12_amd.build_probe import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        log("bench: no libmfma_rate.so (build it with __graft_entry__.build())")
+        return None
+    L = ctypes.CDLL(PROBE_PATH)
+    L.mfma_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.mfma_rate_probe.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wg = 2 * cus                                            # 256 threads each: 8 waves per CU
+    out = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    stamps = torch.zeros(wg * 4, dtype=torch.int64, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+
+    def run():
+        if L.mfma_rate_probe(wg, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stamps.data_ptr()),
+                             ctypes.c_void_p(st)) != 0:
+            raise RuntimeError("mfma_rate_probe failed")
+
+    for _ in range(100):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / launches
+    flops = wg * 4 * iters * 4 * 32768.0
+    tf = flops / t / 1e12
+    s4 = stamps.cpu().view(wg, 4).tolist()
+    mhz = statistics.median((t1 - t0) / ((r1 - r0) / 100e6) / 1e6 for t0, t1, r0, r1 in s4 if r1 > r0)
+    return {"tflops": round(tf, 1), "us_per_launch": round(t * 1e6, 2), "shader_clock_mhz": round(mhz, 1),
+            "flop_per_cu_per_clock": round(tf * 1e12 / (cus * mhz * 1e6), 1), "compute_units": cus,
+            "method": f"libmfma_rate.so: {wg} workgroups x 4 waves, {iters} x 4 independent "
+                      "v_mfma_f32_32x32x16_bf16 per wave; HIP events over "
+                      f"{launches} launches after 100 unmeasured ones; clock = s_memtime ticks per "
+                      "s_memrealtime (100 MHz) tick"}
+
+
 def trace_summary(path, skip):
     """Per-kernel launch statistics from a rocprofv3 kernel trace (CSV), over the launches after the
     first `skip` of each kernel (the warm-up: a fresh process's first launches run at lower clocks).
@@ -253,6 +300,40 @@ def trace_summary(path, skip):
             continue
         print(f"| `{name}` | {len(ts)} | {len(kept)} | {statistics.mean(kept):.1f} | {statistics.median(kept):.1f} | "
               f"{min(kept):.1f} | {max(kept):.1f} |")
+
+
+def clock_summary(prefix, skip):
+    """Per-kernel GFX clock from a rocprofv3 run with --pmc GRBM_COUNT --kernel-trace (CSV output,
+    files PREFIX_counter_collection.csv, PREFIX_kernel_trace.csv, PREFIX_agent_info.csv): GRBM_COUNT
+    counts GFX clocks on every XCD of the dispatch, so clock = GRBM_COUNT / XCDs / duration.  Prints a
+    markdown table over the dispatches after the first `skip` of each kernel; needs no GPU."""
+    import csv
+    import statistics
+    xcc = 1
+    with open(prefix + "_agent_info.csv", newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Agent_Type", "").upper().endswith("GPU") or int(row.get("Num_Xcc") or 0) > 0:
+                xcc = max(xcc, int(row.get("Num_Xcc") or 1))
+    with open(prefix + "_kernel_trace.csv", newline="") as f:
+        span = {r["Dispatch_Id"]: (int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in csv.DictReader(f)}
+    per = {}
+    with open(prefix + "_counter_collection.csv", newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != "GRBM_COUNT" or r["Dispatch_Id"] not in span:
+                continue
+            b, e = span[r["Dispatch_Id"]]
+            if e > b:
+                per.setdefault(r["Kernel_Name"], []).append((b, (e - b) * 1e-9, float(r["Counter_Value"])))
+    print(f"XCDs per dispatch: {xcc}")
+    print("| kernel | dispatches kept | median duration (us) | median clock (MHz) |")
+    print("|---|---|---|---|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+        v = sorted(v)[skip:]
+        if not v:
+            continue
+        short = name[:name.index("(", 1)] if "(" in name[1:] else name
+        print(f"| `{short}` | {len(v)} | {statistics.median(x[1] for x in v) * 1e6:.1f} | "
+              f"{statistics.median(x[2] / xcc / x[1] / 1e6 for x in v):.0f} |")
 
 
 def load_traffic(kernel):
@@ -286,14 +367,22 @@ def main():
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a plain 1 GiB device copy (rocprofv3 counter calibration)")
     ap.add_argument("--no-other", action="store_true", help="skip workloads 2 and 5")
+    ap.add_argument("--no-clock", action="store_true", help="skip the measured matrix-core ceiling")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-kernel statistics of a rocprofv3 kernel trace (no GPU needed) and exit")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="only the matrix-core ceiling probe, then 10 steps of the workload (for clock counters)")
+    ap.add_argument("--clock-summary", metavar="PREFIX",
+                    help="print per-kernel clocks from a rocprofv3 GRBM_COUNT run (no GPU needed) and exit")
     ap.add_argument("--skip", type=int, default=0,
                     help="with --trace-summary: leave out the first SKIP launches of each kernel")
     args = ap.parse_args()
 
     if args.trace_summary:
         trace_summary(args.trace_summary, args.skip)
+        return
+    if args.clock_summary:
+        clock_summary(args.clock_summary, args.skip)
         return
 
     if args.gpus != 1:
@@ -312,6 +401,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": a.numel(), "launches": 3}))
+        return
+
+    if args.probe_only:
+        c = mfma_ceiling(dev, launches=10)
+        w = Workload(CONFIGS[args.config], dev)
+        for _ in range(10):
+            w.step()
+        torch.cuda.synchronize()
+        print(json.dumps({"mfma_ceiling": c}), flush=True)
         return
 
     if args.fp8_only:
@@ -365,6 +463,19 @@ def main():
                 "algorithmic_flop_per_launch": kflops[dom], "avg_launch_us": round(per[dom] * 1e6, 2),
                 "traffic": load_traffic(dom)}
 
+    ceiling = None
+    if not args.no_clock:
+        # the published peak assumes 2.4 GHz on every CU; the chip holds a lower clock under matrix-core
+        # load, so the rate a pure MFMA loop sustains now is a second, measured ceiling
+        ceiling = mfma_ceiling(dev)
+        if ceiling:
+            ceiling["frac_of_ceiling"] = {n: round(kflops[n] / per[n] / 1e12 / ceiling["tflops"], 4) for n in per
+                                          if n in kflops}
+            roofline["measured_mfma_ceiling"] = ceiling["tflops"]
+            roofline["frac_of_measured_ceiling"] = round(achieved / ceiling["tflops"], 4)
+            log(f"bench: MFMA ceiling {ceiling['tflops']} TFLOP/s at {ceiling['shader_clock_mhz']} MHz "
+                f"({ceiling['flop_per_cu_per_clock']} FLOP per CU and clock)")
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True,
@@ -375,6 +486,7 @@ def main():
                    "parallelism": "single GPU"},
         "kernels": kern,
         "roofline": roofline,
+        "mfma_ceiling": ceiling,
         "source_hash": source_hash(),
     }
 

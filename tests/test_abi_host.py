@@ -214,3 +214,25 @@ def test_status_strings():
         assert L.attn_status_str(s)
     assert L.attn_status_str(99) == b"unknown status"
     assert L.attn_last_hip_error() == 0
+
+
+def _probe_lib():
+    from exact_tiled_attention_12_amd.build_probe import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        pytest.fail(f"{PROBE_PATH} is missing: run __graft_entry__.build() first")
+    L = ctypes.CDLL(PROBE_PATH)
+    L.mfma_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.mfma_rate_probe.restype = ctypes.c_int
+    return L
+
+
+def test_probe_header_matches_library():
+    with open(os.path.join(ROOT, "include", "mfma_rate.h")) as f:
+        declared = re.findall(r"^\s*int\s+(\w+)\s*\(", f.read(), re.M)
+    assert declared == ["mfma_rate_probe"]
+    assert hasattr(_probe_lib(), "mfma_rate_probe")
+
+
+@pytest.mark.parametrize("wg,iters,out,stamps", [(0, 1, P, P), (1, 0, P, P), (1, 1, NUL, P), (1, 1, P, NUL)])
+def test_probe_rejects_before_launch(wg, iters, out, stamps):
+    assert _probe_lib().mfma_rate_probe(wg, iters, out, stamps, None) == 1
