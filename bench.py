@@ -233,12 +233,18 @@ def workload_entry(idx, dev, steps, warmup):
     return ent
 
 
-def mfma_ceiling(dev, launches=20, iters=4096):
-    """What the matrix cores sustain now: libmfma_rate.so's pure bf16 MFMA loop (two waves per SIMD,
-    four independent accumulator chains per wave) over every CU, after ~50 ms of the same load so that
-    the clock has settled.  Returns its TFLOP/s (HIP events over `launches` launches), the shader clock
-    from its s_memtime / s_memrealtime stamps (median over workgroups, MHz), and the FLOP per CU and
-    clock those two imply (4096 when the products issue back to back), or None without the probe."""
+PROBE_MIXES = {0: "MFMA only (register operands)", 1: "MFMA fed from LDS (one ds_read_b128 per product)",
+               2: "MFMA + softmax-like VALU (per product: exp of an FMA, a max, an add)",
+               3: "MFMA fed from LDS + softmax-like VALU"}
+
+
+def mfma_ceiling(dev, launches=20, iters=4096, mix=0):
+    """What the matrix cores sustain now: libmfma_rate.so's bf16 MFMA loop (two waves per SIMD, four
+    independent accumulator chains per wave; `mix` adds LDS operand reads and/or softmax-like VALU work)
+    over every CU, after ~50 ms of the same load so that the clock has settled.  Returns its TFLOP/s
+    (HIP events over `launches` launches), the shader clock from its s_memtime / s_memrealtime stamps
+    (median over workgroups, MHz), and the FLOP per CU and clock those two imply (4096 when the
+    products issue back to back), or None without the probe."""
     import ctypes
     import statistics
     from exact_tiled_attention_12_amd.build_probe import PROBE_PATH
@@ -246,7 +252,8 @@ def mfma_ceiling(dev, launches=20, iters=4096):
         log("bench: no libmfma_rate.so (build it with __graft_entry__.build())")
         return None
     L = ctypes.CDLL(PROBE_PATH)
-    L.mfma_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.mfma_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p]
     L.mfma_rate_probe.restype = ctypes.c_int
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     wg = 2 * cus                                            # 256 threads each: 8 waves per CU
@@ -255,7 +262,7 @@ def mfma_ceiling(dev, launches=20, iters=4096):
     st = torch.cuda.current_stream(dev).cuda_stream
 
     def run():
-        if L.mfma_rate_probe(wg, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stamps.data_ptr()),
+        if L.mfma_rate_probe(wg, iters, mix, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stamps.data_ptr()),
                              ctypes.c_void_p(st)) != 0:
             raise RuntimeError("mfma_rate_probe failed")
 
@@ -274,6 +281,7 @@ def mfma_ceiling(dev, launches=20, iters=4096):
     mhz = statistics.median((t1 - t0) / ((r1 - r0) / 100e6) / 1e6 for t0, t1, r0, r1 in s4 if r1 > r0)
     return {"tflops": round(tf, 1), "us_per_launch": round(t * 1e6, 2), "shader_clock_mhz": round(mhz, 1),
             "flop_per_cu_per_clock": round(tf * 1e12 / (cus * mhz * 1e6), 1), "compute_units": cus,
+            "mix": PROBE_MIXES[mix],
             "method": f"libmfma_rate.so: {wg} workgroups x 4 waves, {iters} x 4 independent "
                       "v_mfma_f32_32x32x16_bf16 per wave; HIP events over "
                       f"{launches} launches after 100 unmeasured ones; clock = s_memtime ticks per "
@@ -331,7 +339,14 @@ def clock_summary(prefix, skip):
         v = sorted(v)[skip:]
         if not v:
             continue
-        short = name[:name.index("(", 1)] if "(" in name[1:] else name
+        short = name
+        if name.endswith(")"):                 # drop the parameter list (the last balanced parentheses)
+            depth = 0
+            for i in range(len(name) - 1, -1, -1):
+                depth += {")": 1, "(": -1}.get(name[i], 0)
+                if depth == 0:
+                    short = name[:i]
+                    break
         print(f"| `{short}` | {len(v)} | {statistics.median(x[1] for x in v) * 1e6:.1f} | "
               f"{statistics.median(x[2] / xcc / x[1] / 1e6 for x in v):.0f} |")
 
@@ -404,12 +419,16 @@ def main():
         return
 
     if args.probe_only:
-        c = mfma_ceiling(dev, launches=10)
+        res = []
+        for mix in PROBE_MIXES:
+            res.append(mfma_ceiling(dev, launches=10, mix=mix))
+            log(f"bench: probe mix {mix} ({PROBE_MIXES[mix]}): {res[-1]['tflops']} TFLOP/s at "
+                f"{res[-1]['shader_clock_mhz']} MHz ({res[-1]['flop_per_cu_per_clock']} FLOP per CU and clock)")
         w = Workload(CONFIGS[args.config], dev)
         for _ in range(10):
             w.step()
         torch.cuda.synchronize()
-        print(json.dumps({"mfma_ceiling": c}), flush=True)
+        print(json.dumps({"mfma_probe": res}), flush=True)
         return
 
     if args.fp8_only:
@@ -467,14 +486,22 @@ def main():
     if not args.no_clock:
         # the published peak assumes 2.4 GHz on every CU; the chip holds a lower clock under matrix-core
         # load, so the rate a pure MFMA loop sustains now is a second, measured ceiling
+        # (mix 0); and what a dependency-free loop with the attention loop's work per product (an LDS operand
+        # read, an exponential and three other VALU instructions) sustains (mix 3)
         ceiling = mfma_ceiling(dev)
-        if ceiling:
-            ceiling["frac_of_ceiling"] = {n: round(kflops[n] / per[n] / 1e12 / ceiling["tflops"], 4) for n in per
-                                          if n in kflops}
+        mixed = mfma_ceiling(dev, mix=3) if ceiling else None
+        if ceiling and mixed:
+            for c_ in (ceiling, mixed):
+                c_["frac_of_ceiling"] = {n: round(kflops[n] / per[n] / 1e12 / c_["tflops"], 4) for n in per
+                                         if n in kflops}
+            ceiling["with_attention_mix"] = mixed
             roofline["measured_mfma_ceiling"] = ceiling["tflops"]
             roofline["frac_of_measured_ceiling"] = round(achieved / ceiling["tflops"], 4)
+            roofline["measured_mixed_ceiling"] = mixed["tflops"]
+            roofline["frac_of_mixed_ceiling"] = round(achieved / mixed["tflops"], 4)
             log(f"bench: MFMA ceiling {ceiling['tflops']} TFLOP/s at {ceiling['shader_clock_mhz']} MHz "
-                f"({ceiling['flop_per_cu_per_clock']} FLOP per CU and clock)")
+                f"({ceiling['flop_per_cu_per_clock']} FLOP per CU and clock); with the attention loop's mix "
+                f"{mixed['tflops']} TFLOP/s at {mixed['shader_clock_mhz']} MHz")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -221,7 +221,8 @@ def _probe_lib():
     if not os.path.exists(PROBE_PATH):
         pytest.fail(f"{PROBE_PATH} is missing: run __graft_entry__.build() first")
     L = ctypes.CDLL(PROBE_PATH)
-    L.mfma_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.mfma_rate_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p]
     L.mfma_rate_probe.restype = ctypes.c_int
     return L
 
@@ -233,6 +234,7 @@ def test_probe_header_matches_library():
     assert hasattr(_probe_lib(), "mfma_rate_probe")
 
 
-@pytest.mark.parametrize("wg,iters,out,stamps", [(0, 1, P, P), (1, 0, P, P), (1, 1, NUL, P), (1, 1, P, NUL)])
-def test_probe_rejects_before_launch(wg, iters, out, stamps):
-    assert _probe_lib().mfma_rate_probe(wg, iters, out, stamps, None) == 1
+@pytest.mark.parametrize("wg,iters,mix,out,stamps", [(0, 1, 0, P, P), (1, 0, 0, P, P), (1, 1, -1, P, P), (1, 1, 4, P, P),
+                                                   (1, 1, 0, NUL, P), (1, 1, 0, P, NUL)])
+def test_probe_rejects_before_launch(wg, iters, mix, out, stamps):
+    assert _probe_lib().mfma_rate_probe(wg, iters, mix, out, stamps, None) == 1
