@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 import torch  # noqa: E402
 
 from exact_tiled_attention_12_amd import (attn_bwd_blocksparse, attn_bwd_dkdv, attn_bwd_dq_d,  # noqa: E402
-                                          attn_fwd, attn_fwd_blocksparse, attn_fwd_fp8)
+                                          attn_fwd, attn_fwd_blocksparse, attn_fwd_fp8, prepare)
 from exact_tiled_attention_12_amd.configs import CONFIGS  # noqa: E402
 from exact_tiled_attention_12_amd.flops import attn_flops, blocksparse_flops  # noqa: E402
 from exact_tiled_attention_12_amd.inputs import config_inputs, local_global_mask, make_fp8_inputs  # noqa: E402
@@ -69,21 +69,27 @@ class Workload:
         self.dv = torch.empty_like(self.dq)
         self.fl_fwd = attn_flops(B, H, N, d, cfg.causal, "fwd")
         self.fl_bwd = attn_flops(B, H, N, d, cfg.causal, "bwd")
+        # each entry point's arguments checked and marshalled once (prepare): a step re-issues the same
+        # C calls on the current stream, so that the host's per-call Python work does not leave the GPU
+        # idle between short kernels (the d = 64 forward runs 41 us, about what those checks take)
+        c = cfg
+        self.launch = [prepare(attn_fwd, self.q, self.k, self.v, causal=c.causal, out=self.o, lse=self.lse)[0]]
+        if c.backward:
+            self.launch += [
+                prepare(attn_bwd_dq_d, self.q, self.k, self.v, self.o, self.do, self.lse, D=self.D, causal=c.causal,
+                        dq=self.dq)[0],
+                prepare(attn_bwd_dkdv, self.q, self.k, self.v, self.do, self.lse, self.D, causal=c.causal,
+                        dk=self.dk, dv=self.dv)[0]]
 
     KERNELS = ("attn_fwd", "attn_bwd_dq_d", "attn_bwd_dkdv")
 
     def step(self, ev=None):
-        c = self.cfg
-        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
-        rec(0)
-        attn_fwd(self.q, self.k, self.v, causal=c.causal, out=self.o, lse=self.lse)
-        rec(1)
-        if not c.backward:
-            return
-        attn_bwd_dq_d(self.q, self.k, self.v, self.o, self.do, self.lse, D=self.D, causal=c.causal, dq=self.dq)
-        rec(2)
-        attn_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.D, causal=c.causal, dk=self.dk, dv=self.dv)
-        rec(3)
+        if ev is not None:
+            ev[0].record()
+        for i, launch in enumerate(self.launch):
+            launch()
+            if ev is not None:
+                ev[i + 1].record()
 
     def measure(self, steps, warmup):
         """Returns (wall seconds per step, {kernel: mean seconds per launch})."""
@@ -212,9 +218,17 @@ def workload_entry(idx, dev, steps, warmup):
     (algorithmic FLOPs: 4 N^2 d per head forward, the backward's 2.5x split as in main())."""
     cfg = CONFIGS[idx]
     w = Workload(cfg, dev)
+    # the clocks take ~30 ms of load to settle: a short workload gets at least enough warm-up steps
+    # to cover 60 ms (30 steps of the d = 64 forward are only ~1.5 ms)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        w.step()
+    torch.cuda.synchronize()
+    warmup = max(warmup, int(0.06 / ((time.perf_counter() - t0) / 5)) + 1)
     wall, per = w.measure(steps, warmup)
     kflops = {"attn_fwd": w.fl_fwd, "attn_bwd_dkdv": 2.0 * w.fl_fwd, "attn_bwd_dq_d": 0.5 * w.fl_fwd}
-    ent = {"workload": f"{cfg.name} (seed {cfg.seed})", "steps": steps, "ms_per_step": round(wall * 1e3, 4),
+    ent = {"workload": f"{cfg.name} (seed {cfg.seed})", "steps": steps, "warmup": warmup,
+           "ms_per_step": round(wall * 1e3, 4),
            "kernels": {n: {"us": round(t * 1e6, 2), "tflops": round(kflops[n] / t / 1e12, 2),
                            "frac_peak": round(kflops[n] / t / 1e12 / PEAK_BF16_TFLOPS, 4)} for n, t in per.items()},
            "fwd_tflops": round(w.fl_fwd / per["attn_fwd"] / 1e12, 2),

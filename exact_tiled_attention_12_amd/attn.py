@@ -87,7 +87,14 @@ def _dt(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+# While prepare() runs a binding function, its C calls are recorded here instead of made, with
+# every tensor whose pointer they carry (so that those buffers outlive the prepared launch).
+_recording = None
+
+
 def _ptr(t):
+    if t is not None and _recording is not None:
+        _recording[1].append(t)
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
@@ -143,9 +150,38 @@ def _workspace(workspace, need, dev):
 
 
 def _call(name, *args):
+    if _recording is not None:
+        _recording[0].append((getattr(lib(), name), name, args))
+        return
     st = getattr(lib(), name)(*args)
     if st != ATTN_OK:
         raise AttnError(st, name)
+
+
+def prepare(fn, *args, **kwargs):
+    """Checks and marshals one call of a binding function (attn_fwd, attn_bwd, attn_bwd_dq_d, ...)
+    once, without launching anything, and returns (launch, result).  launch() re-issues exactly
+    the C calls that fn would have made: same buffers, same scalars, same stream, status checked.
+    It skips the per-call Python checks, which cost more than a short kernel runs (a loop that
+    enqueues one fixed launch many times otherwise keeps the GPU waiting on the host).  result is
+    what fn returned (its output tensors); launch keeps every buffer the calls use alive."""
+    global _recording
+    if _recording is not None:
+        raise RuntimeError("prepare() does not nest")
+    _recording = ([], [])
+    try:
+        result = fn(*args, **kwargs)
+        calls, keep = _recording
+    finally:
+        _recording = None
+
+    def launch():
+        for f, name, cargs in calls:
+            st = f(*cargs)
+            if st != ATTN_OK:
+                raise AttnError(st, name)
+    launch.buffers = keep
+    return launch, result
 
 
 def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):

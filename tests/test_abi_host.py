@@ -238,3 +238,14 @@ def test_probe_header_matches_library():
                                                    (1, 1, 0, NUL, P), (1, 1, 0, P, NUL)])
 def test_probe_rejects_before_launch(wg, iters, mix, out, stamps):
     assert _probe_lib().mfma_rate_probe(wg, iters, mix, out, stamps, None) == 1
+
+
+def test_prepare_checks_like_the_call_and_leaves_no_recording():
+    import torch
+    q = _t((1, 2, 40, 64))
+    with pytest.raises(ValueError, match="must"):
+        attn.prepare(attn.attn_fwd, q, _t((1, 2, 41, 64)), q)
+    assert attn._recording is None
+    with pytest.raises(ValueError, match="GPU"):
+        attn.prepare(attn.attn_fwd, q, q, q, out=torch.zeros_like(q))
+    assert attn._recording is None

@@ -17,8 +17,8 @@ import pytest
 import torch
 
 import oracle
-from exact_tiled_attention_12_amd import (attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_main, attn_bwd_preprocess,
-                                          attn_fwd)
+from exact_tiled_attention_12_amd import (attn_bwd, attn_bwd_dkdv, attn_bwd_dq, attn_bwd_dq_d, attn_bwd_main,
+                                          attn_bwd_preprocess, attn_fwd, prepare)
 from exact_tiled_attention_12_amd.inputs import make_inputs
 
 from bf16_bound import bounds as bf16_bounds
@@ -145,3 +145,32 @@ def test_more_than_2_31_elements():
     # every head written: no NaN left anywhere (checked on the device)
     for t in (o, lse, dq, dk, dv):
         assert not torch.isnan(t).any()
+
+
+def test_prepared_launches_match_direct_calls():
+    """prepare() marshals a call once and launches nothing; each launch() then gives the same bits as
+    the direct call (the bf16 kernels are deterministic), also into outputs prepare() allocated."""
+    dev = _dev()
+    _say("case prepared launches: B=2 H=3 N=300 d=128 causal bf16")
+    q, k, v, do = (t.to(dev) for t in make_inputs(2, 3, 300, 128, "bf16", seed=31))
+    o_ref, l_ref = attn_fwd(q, k, v, causal=True)
+    D_ref = torch.empty_like(l_ref)
+    dq_ref, _ = attn_bwd_dq_d(q, k, v, o_ref, do, l_ref, D=D_ref, causal=True)
+    dk_ref, dv_ref = attn_bwd_dkdv(q, k, v, do, l_ref, D_ref, causal=True)
+    o, lse, D, dq, dk, dv = (_nan_like(t, t.dtype) for t in (o_ref, l_ref, D_ref, dq_ref, dk_ref, dv_ref))
+    fwd, _ = prepare(attn_fwd, q, k, v, causal=True, out=o, lse=lse)
+    qside, _ = prepare(attn_bwd_dq_d, q, k, v, o, do, lse, D=D, causal=True, dq=dq)
+    kside, _ = prepare(attn_bwd_dkdv, q, k, v, do, lse, D, causal=True, dk=dk, dv=dv)
+    fwd2, (o2, l2) = prepare(attn_fwd, q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(o.float()).all() and torch.isnan(dq).all() and torch.isnan(dk).all()
+    for rep in range(3):
+        fwd()
+        qside()
+        kside()
+        fwd2()
+        torch.cuda.synchronize()
+        for name, a, b in (("O", o, o_ref), ("LSE", lse, l_ref), ("D", D, D_ref), ("dQ", dq, dq_ref),
+                           ("dK", dk, dk_ref), ("dV", dv, dv_ref), ("O (allocated)", o2, o_ref),
+                           ("LSE (allocated)", l2, l_ref)):
+            assert torch.equal(a, b), f"launch {rep}: {name} differs from the direct call"
