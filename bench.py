@@ -54,6 +54,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def warm(run, steps, min_seconds):
+    """Runs `run` at least `steps` times and until `min_seconds` of load have passed: the GPU's clocks
+    take about 30 ms of load to settle, and a short workload's fixed step count covers less.  Returns
+    the number of runs."""
+    n, t0 = 0, time.perf_counter()
+    while n < steps:
+        run()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(5):
+            run()
+        n += 5
+        torch.cuda.synchronize()
+    return n
+
+
 class Workload:
     def __init__(self, cfg, dev):
         self.cfg = cfg
@@ -91,11 +108,10 @@ class Workload:
             if ev is not None:
                 ev[i + 1].record()
 
-    def measure(self, steps, warmup):
-        """Returns (wall seconds per step, {kernel: mean seconds per launch})."""
-        for _ in range(warmup):
-            self.step()
-        torch.cuda.synchronize()
+    def measure(self, steps, warmup, min_warm_seconds=0.0):
+        """Returns (wall seconds per step, {kernel: mean seconds per launch}), after `warmup` steps
+        (and at least `min_warm_seconds` of them)."""
+        self.warmup_done = warm(self.step, warmup, min_warm_seconds)
         # wall clock over exactly `steps` steps, synchronised on both sides
         t0 = time.perf_counter()
         for _ in range(steps):
@@ -150,9 +166,7 @@ class SparseWorkload:
             ev[2].record()
 
     def measure(self, steps, warmup):
-        for _ in range(warmup):
-            self.step()
-        torch.cuda.synchronize()
+        self.warmup_done = warm(self.step, warmup, 0.06)
         t0 = time.perf_counter()
         for _ in range(steps):
             self.step()
@@ -174,10 +188,8 @@ def fp8_forward(cfg, dev, steps, warmup):
     q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(q8.shape[:-1], dtype=torch.float32, device=dev)
-    run = lambda: attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=cfg.causal, out=o, lse=lse)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
+    run = prepare(attn_fwd_fp8, q8, k8, v8, sq, sk, sv, causal=cfg.causal, out=o, lse=lse)[0]
+    warm(run, warmup, 0.06)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -218,14 +230,8 @@ def workload_entry(idx, dev, steps, warmup):
     (algorithmic FLOPs: 4 N^2 d per head forward, the backward's 2.5x split as in main())."""
     cfg = CONFIGS[idx]
     w = Workload(cfg, dev)
-    # the clocks take ~30 ms of load to settle: a short workload gets at least enough warm-up steps
-    # to cover 60 ms (30 steps of the d = 64 forward are only ~1.5 ms)
-    t0 = time.perf_counter()
-    for _ in range(5):
-        w.step()
-    torch.cuda.synchronize()
-    warmup = max(warmup, int(0.06 / ((time.perf_counter() - t0) / 5)) + 1)
-    wall, per = w.measure(steps, warmup)
+    wall, per = w.measure(steps, warmup, 0.06)    # warm-up of at least 60 ms (30 steps of workload 2: ~1.5 ms)
+    warmup = w.warmup_done
     kflops = {"attn_fwd": w.fl_fwd, "attn_bwd_dkdv": 2.0 * w.fl_fwd, "attn_bwd_dq_d": 0.5 * w.fl_fwd}
     ent = {"workload": f"{cfg.name} (seed {cfg.seed})", "steps": steps, "warmup": warmup,
            "ms_per_step": round(wall * 1e3, 4),
@@ -538,7 +544,7 @@ def main():
         log("bench: secondary workload 4 (N=16384)")
         w4 = Workload(cfg4, dev)
         steps4 = max(3, args.steps // 2)
-        wall4, per4 = w4.measure(steps4, max(2, args.warmup // 2))
+        wall4, per4 = w4.measure(steps4, max(2, args.warmup // 2), 0.06)
         tb4 = sum(t for n, t in per4.items() if n != "attn_fwd")
         out["secondary"] = {
             "workload": "B=1 H=16 N=16384 d=128 causal bf16 (Q,K x0.5)", "steps": steps4,
