@@ -149,7 +149,8 @@ def test_more_than_2_31_elements():
 
 def test_prepared_launches_match_direct_calls():
     """prepare() marshals a call once and launches nothing; each launch() then gives the same bits as
-    the direct call (the bf16 kernels are deterministic), also into outputs prepare() allocated."""
+    the direct call (the bf16 kernels are deterministic), also into outputs prepare() allocated and
+    with a workspace the binding allocated inside the call."""
     dev = _dev()
     _say("case prepared launches: B=2 H=3 N=300 d=128 causal bf16")
     q, k, v, do = (t.to(dev) for t in make_inputs(2, 3, 300, 128, "bf16", seed=31))
@@ -164,12 +165,23 @@ def test_prepared_launches_match_direct_calls():
     fwd2, (o2, l2) = prepare(attn_fwd, q, k, v, causal=True)
     torch.cuda.synchronize()
     assert torch.isnan(o.float()).all() and torch.isnan(dq).all() and torch.isnan(dk).all()
+    # attn_bwd with no workspace: the binding allocates one inside the call, kept alive by the launch
+    full, grads = prepare(attn_bwd, q, k, v, o_ref, do, l_ref, causal=True)
+    grads_ref = attn_bwd(q, k, v, o_ref, do, l_ref, causal=True)
+    for g in grads:
+        g.fill_(float("nan"))
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
     for rep in range(3):
         fwd()
         qside()
         kside()
         fwd2()
+        full()
         torch.cuda.synchronize()
+        for name, a, b in zip(("dQ (attn_bwd)", "dK (attn_bwd)", "dV (attn_bwd)"), grads, grads_ref):
+            assert torch.equal(a, b), f"launch {rep}: {name} differs from the direct call"
         for name, a, b in (("O", o, o_ref), ("LSE", lse, l_ref), ("D", D, D_ref), ("dQ", dq, dq_ref),
                            ("dK", dk, dk_ref), ("dV", dv, dv_ref), ("O (allocated)", o2, o_ref),
                            ("LSE (allocated)", l2, l_ref)):
